@@ -1,0 +1,37 @@
+"""fp64 CPU oracle for index-gathered sparse attention (TEST INFRASTRUCTURE).
+
+This package is a plain, slow, obviously correct restatement of what the
+GPU library computes. Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import it; the library and its Python binding never
+do, and this package imports nothing from them. Its inputs come from the
+seeded generators in ``gen`` (random draws only, no method arithmetic).
+
+Modules
+-------
+attention   per-token sparse attention and ragged chunk prefill
+union       union-of-G index build (sorted, deduplicated, ownership bits) and
+            union attention
+pages       decode-pool page mark and (masked) page split
+
+Every function cites the passage of the pages it restates. Where the pages
+leave a point open, the reading taken is stated at the function.
+
+Parity status: every function here is pinned by CPU tests against
+definitions outside this package (dense float64 attention in torch, mpmath
+brute force, closed forms, Python-set semantics, numpy reshapes); none is
+"parity unpinned".
+"""
+from .attention import bf16_to_f64, sparse_attention, chunk_prefill, row_attention
+from .union import union_build, union_attention
+from .pages import page_mark, page_split
+
+__all__ = [
+    "bf16_to_f64",
+    "sparse_attention",
+    "chunk_prefill",
+    "row_attention",
+    "union_build",
+    "union_attention",
+    "page_mark",
+    "page_split",
+]

@@ -1,0 +1,90 @@
+"""Union-of-G index sets and union attention in fp64 (TEST INFRASTRUCTURE:
+oracle only).
+
+sglang PR 32779, "Modifications" (``--dsa-triton-union``): G adjacent tokens
+share one gathered index set; a per-row ownership bitmask restores each
+token's own softmax support, so the result equals the per-token path. The set
+is built per group: each token's rows are sorted on their own, then a token
+emits a row if no earlier token of the group selected it, and every token
+that selected a row sets its bit. The accuracy section adds the contract:
+each row once, bits equal to the OR of its owners, -1 dropped.
+
+Canonical layout (the pages fix the membership, not the storage; this is the
+reading the library follows):
+
+* group g covers rows g*G .. min(g*G+G, T)-1; the last group of a T % G != 0
+  batch simply has fewer members, and absent members own nothing;
+* union_idx[g] lists token 0's distinct valid indices ascending, then token
+  1's indices that token 0 lacks, ascending, and so on; then -1 fill;
+* union_bits[g, r] has bit j set iff member j selected union_idx[g, r]
+  (bit 0 = the group's first token); 0 fill;
+* union_len[g] is the number of listed rows;
+* an index is valid iff 0 <= x < kv_len; duplicates within one token's row
+  collapse to one entry.
+"""
+from __future__ import annotations
+
+from typing import Tuple
+
+import numpy as np
+
+from .attention import bf16_to_f64, row_attention
+
+
+def union_build(idx: np.ndarray, kv_len: int, G: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Returns union_idx int32 [ceil(T/G), G*k], union_bits uint8 [same],
+    union_len int32 [ceil(T/G)]."""
+    T, k = idx.shape
+    n_groups = (T + G - 1) // G
+    union_idx = np.full((n_groups, G * k), -1, dtype=np.int32)
+    union_bits = np.zeros((n_groups, G * k), dtype=np.uint8)
+    union_len = np.zeros(n_groups, dtype=np.int32)
+    for g in range(n_groups):
+        members = range(g * G, min(g * G + G, T))
+        sets = []
+        for t in members:
+            sets.append({int(x) for x in idx[t] if 0 <= int(x) < kv_len})
+        emitted = []
+        earlier = set()
+        for s in sets:
+            for x in sorted(s):
+                if x not in earlier:
+                    emitted.append(x)
+            earlier |= s
+        for r, x in enumerate(emitted):
+            bits = 0
+            for j, s in enumerate(sets):
+                if x in s:
+                    bits |= 1 << j
+            union_idx[g, r] = x
+            union_bits[g, r] = bits
+        union_len[g] = len(emitted)
+    return union_idx, union_bits, union_len
+
+
+def union_attention(q: np.ndarray, k: np.ndarray, v, union_idx: np.ndarray,
+                    union_bits: np.ndarray, union_len: np.ndarray, G: int, *,
+                    num_kv_heads: int, scale: float, head_dim_v=None,
+                    rows=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of each token over the union rows whose ownership bit it
+    holds (PR 32779, "Modifications"). Same per-(row, head) definition as
+    the per-token oracle, with the support taken from the union set."""
+    T, Hq, _ = q.shape
+    group = Hq // num_kv_heads
+    dv = head_dim_v if v is None else v.shape[2]
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    out = np.zeros((len(rows), Hq, dv))
+    lse = np.zeros((len(rows), Hq))
+    for r, t in enumerate(rows):
+        g, j = divmod(int(t), G)
+        n = int(union_len[g])
+        own = (union_bits[g, :n] >> j) & 1
+        tok = union_idx[g, :n][own.astype(bool)].astype(np.int64)
+        for kvh in range(num_kv_heads):
+            kr = bf16_to_f64(k[tok, kvh, :])
+            vr = kr[:, :dv] if v is None else bf16_to_f64(v[tok, kvh, :])
+            heads = slice(kvh * group, (kvh + 1) * group)
+            o, s = row_attention(bf16_to_f64(q[t, heads, :]), kr, vr, scale)
+            out[r, heads] = o
+            lse[r, heads] = s
+    return out, lse
