@@ -1,0 +1,255 @@
+"""Benchmark: sparse GQA chunk prefill, 8192 rows x 2051 slots, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 10]
+
+One step is one sparse_attn_chunk_prefill call over the 8192-row workload
+(one request at the end of a 32768-token context, top-k 2051 random-walk
+indices, 6 query heads over one KV head, head dim 256, bf16 inputs, fp32
+output and log-sum-exp), with every input already resident in HBM.
+
+Prints one JSON line. `value` is the gathered-KV throughput: the K and V rows
+of every valid slot (8192 * 2051 * (512 + 512) B = 17.205 GB per call)
+divided by the measured time per call. `roofline.achieved` is the same
+algorithmic byte count divided by the kernel's average duration, measured
+with HIP events on the stream the kernel is launched on; it is compared with
+MI355X's 8 TB/s HBM3E peak (gathered bytes can exceed HBM traffic when rows
+repeat in cache; `roofline.traffic` holds the measured HBM bytes per call from
+rocprofv3 counters when they were taken on the current kernel source).
+
+The CPU baseline runs the fp64 oracle on a bounded sample of the same
+workload's rows, in worker processes started before the GPU is touched, and
+its results double as a parity gate on those rows.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import gen  # noqa: E402
+
+METRIC = "sparse prefill ms/call + gathered-KV GB/s (% HBM roofline), 8192 rows × 2051 slots"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "top_index_sparse_amd", "csrc", "sa_gqa.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gqa_d256_c1_traffic.txt")
+
+
+def gathered_bytes(case: gen.AttnCase) -> int:
+    """K and V bytes of every valid slot (one KV head per query group)."""
+    if case.cu_seqlens_q is None:
+        valid = int(((case.idx >= 0) & (case.idx < case.kv_len)).sum())
+    else:
+        valid = 0
+        for r in range(len(case.cu_seqlens_q) - 1):
+            rows = slice(case.cu_seqlens_q[r], case.cu_seqlens_q[r + 1])
+            kv = case.cu_seqlens_kv[r + 1] - case.cu_seqlens_kv[r]
+            blk = case.idx[rows]
+            valid += int(((blk >= 0) & (blk < kv)).sum())
+    per_slot = case.head_dim_qk * 2 + (0 if case.v_in_k else case.head_dim_v * 2)
+    return valid * case.num_kv_heads * per_slot
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("sa_gqa.hip", "sa_device.h", "sa_internal.h"):
+        with open(os.path.join(ROOT, "top_index_sparse_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per call measured by rocprofv3 counters, if they were taken
+    on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(l.split(":", 1) for l in f if ":" in l)
+        if kv.get("kernel_source_sha256_16", "").strip() != kernel_source_hash():
+            return None
+        return float(kv["hbm_bytes_per_call"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------- CPU baseline
+
+_CASE = None
+
+
+def _cpu_worker(rows):
+    from threadpoolctl import threadpool_limits
+    import oracle
+    with threadpool_limits(1):
+        c = _CASE
+        o, l = oracle.sparse_attention(c.q, c.k, c.v, c.idx, num_kv_heads=c.num_kv_heads,
+                                       scale=c.scale, kv_len=c.kv_len, rows=rows)
+    return rows, o.astype(np.float32), l
+
+
+def cpu_baseline(case: gen.AttnCase, stride: int, workers: int):
+    """The oracle over every `stride`-th row, split over `workers` processes."""
+    import multiprocessing as mp
+    global _CASE
+    _CASE = case
+    rows = np.arange(0, case.num_rows, stride)
+    chunks = [c for c in np.array_split(rows, workers * 4) if len(c)]
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        parts = pool.map(_cpu_worker, chunks)
+    wall = time.perf_counter() - t0
+    sub = gen.AttnCase(case.name, case.q, case.k, case.v, case.idx[rows], case.num_kv_heads,
+                       case.head_dim_qk, case.head_dim_v, case.scale, case.kv_len,
+                       case.positions[rows])
+    nbytes = gathered_bytes(sub)
+    out_rows = np.concatenate([p[0] for p in parts])
+    out_o = np.concatenate([p[1] for p in parts])
+    out_l = np.concatenate([p[2] for p in parts])
+    return {"value": nbytes / wall / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": f"every {stride}th row of the same workload ({len(rows)} of "
+                      f"{case.num_rows} rows, {nbytes / 1e9:.3f} GB gathered), fp64 numpy, "
+                      f"{workers} processes x 1 BLAS thread, {wall:.2f} s wall"}, \
+        (out_rows, out_o, out_l)
+
+
+# ------------------------------------------------------------------- GPU
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on",
+                    help="off for profiler runs (the profiler initialises the GPU before "
+                         "the program, so no worker processes may be forked)")
+    ap.add_argument("--cpu-stride", type=int, default=2)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (to scale HBM counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(rows and KV heads shard with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_probe:
+        import torch
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n}))
+        return
+
+    case = gen.make_config("C1", args.seed)
+    nbytes = gathered_bytes(case)
+
+    cpu, cpu_out = None, None
+    if args.cpu_baseline == "on":
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        cpu, cpu_out = cpu_baseline(case, args.cpu_stride, workers)
+
+    import torch
+    import top_index_sparse_amd as sa
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = bf16(case.q), bf16(case.k), bf16(case.v)
+    idx = torch.from_numpy(case.idx).cuda()
+    cu_q = torch.tensor([0, case.num_rows], dtype=torch.int32, device="cuda")
+    cu_kv = torch.tensor([0, case.kv_len], dtype=torch.int64, device="cuda")
+    out = torch.empty((case.num_rows, case.num_q_heads, case.head_dim_v), dtype=torch.float32,
+                      device="cuda")
+    lse = torch.empty((case.num_rows, case.num_q_heads), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        sa.sparse_attn_chunk_prefill(q, k, v, idx, cu_q, cu_kv, total_q=case.num_rows,
+                                     sm_scale=case.scale, out=out, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    calls0 = sa.sa_call_count("sparse_attn_chunk_prefill")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert sa.sa_call_count("sparse_attn_chunk_prefill") - calls0 == args.steps
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    ms = wall * 1e3 / args.steps
+
+    parity = None
+    if cpu_out is not None:
+        rows, ro, rl = cpu_out
+        sel = torch.from_numpy(rows).cuda()
+        go = out[sel].cpu().numpy().astype(np.float64)
+        gl = lse[sel].cpu().numpy().astype(np.float64)
+        err = np.abs(go - ro)
+        ok = bool(np.all(err <= 2e-2 + 1e-2 * np.abs(ro)) and np.abs(gl - rl).max() <= 1e-5)
+        parity = {"rows_checked": int(len(rows)), "max_abs_err_out": float(err.max()),
+                  "max_abs_err_lse": float(np.abs(gl - rl).max()), "pass": ok}
+        if not ok:
+            print(json.dumps({"parity": parity}), file=sys.stderr)
+            sys.exit(1)
+
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    valid_slots = nbytes // 1024
+    tflops = 2.0 * case.num_q_heads * valid_slots * (case.head_dim_qk + case.head_dim_v) \
+        / (kernel_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(nbytes / (ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "sparse GQA chunk prefill: 8192 query rows at the end of a "
+                        "32768-token context, top-k 2051 random-walk indices, 6 query "
+                        "heads over 1 KV head, head dim 256, bf16 in, fp32 out + LSE",
+            "rows": case.num_rows, "topk": case.topk, "kv_len": case.kv_len,
+            "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
+            "head_dim": case.head_dim_qk, "seed": args.seed,
+            "gathered_bytes_per_call": nbytes,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(),
+        },
+        "cpu_baseline": cpu,
+        "kernel_ms": round(kernel_ms, 4),
+        "tflops_useful": round(tflops, 2),
+        "parity": parity,
+    }
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,237 @@
+/*
+ * sparse_attn.h -- C ABI of the index-gathered sparse attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes, on the caller's HIP stream:
+ *   - per-token sparse attention forward: every query row gathers its own
+ *     top-k KV slots (int32 token indices, -1 = padding), scores them against
+ *     the query heads of one GQA group (or MLA head set), and writes the
+ *     softmax-weighted sum of the gathered V rows plus the log-sum-exp;
+ *   - the same over ragged requests with cached prefixes (chunk prefill);
+ *   - union mode: G adjacent rows share one sorted, deduplicated index set
+ *     with per-row ownership bits that restore each row's own support;
+ *   - the decode-pool page mark and (masked) page split.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are owned by the caller. The library allocates and
+ *     frees nothing, keeps no state between calls except call counters and
+ *     the last error message, and never reads device memory from the host.
+ *   - Work is enqueued on `stream` and returns without synchronising; the
+ *     grids depend on host scalars only, so every call can be captured in a
+ *     HIP graph.
+ *   - Argument errors are reported before anything is launched; a launch
+ *     failure returns SA_ERR_HIP. sa_last_error() describes the last error
+ *     of the calling thread.
+ *   - bf16 tensors (q, k, v) need 16-byte aligned base pointers and row
+ *     strides that are multiples of 8 elements; fp32 outputs need 16-byte
+ *     aligned base pointers and row strides that are multiples of 4.
+ *   - An index x of a row is valid iff 0 <= x < kv_len (kv_len of the row's
+ *     request). Invalid slots are never dereferenced and contribute nothing.
+ *     A row with no valid slot gets O = 0 and LSE = -inf.
+ *   - Duplicated indices in one row count with multiplicity on the
+ *     per-token paths (sglang PR 32779, "Accuracy Tests": a duplicated row
+ *     is weighted twice); union mode deduplicates them (each row once).
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  /* Union tile illegal for this head group (G * group > 32): the per-token
+   * result was computed instead (sglang PR 32779, review item 1: an illegal
+   * union tile falls back to the per-token path). */
+  SA_OK_FALLBACK = 1,
+  SA_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  SA_ERR_SHAPE = -2,       /* sizes, strides or alignment not acceptable    */
+  SA_ERR_DTYPE = -3,       /* KV dtype other than bf16 (PR 32779,
+                              "Robustness": the wrapper refuses a non-bf16 KV
+                              cache instead of reading packed FP8 bytes)    */
+  SA_ERR_UNSUPPORTED = -4, /* valid but not built (head dims, group size)   */
+  SA_ERR_WORKSPACE = -5,   /* workspace missing or too small                */
+  SA_ERR_HIP = -6          /* the HIP runtime reported an error             */
+} sa_status;
+
+typedef enum { SA_DTYPE_BF16 = 1, SA_DTYPE_FP8_E4M3 = 2 } sa_dtype;
+
+/* Shape of one attention call.
+ *
+ * Layouts (elements, row-major):
+ *   q   [rows][num_q_heads][head_dim_qk]      row stride q_row_stride
+ *   k   [tokens][num_kv_heads][head_dim_qk]   row stride kv_row_stride
+ *   v   [tokens][num_kv_heads][head_dim_v]    row stride v_row_stride
+ *       (v_in_k = 1: V is the first head_dim_v columns of each K row, the
+ *        MLA latent row of PR 32779 "Speed Tests": 576 wide, 512 used as V;
+ *        the v pointer is then ignored)
+ *   idx [rows][topk] int32                    row stride idx_row_stride
+ *   out [rows][num_q_heads][head_dim_v] fp32  row stride out_row_stride
+ *   lse [rows][num_q_heads] fp32, contiguous, natural log
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * Built shapes: (head_dim_qk, head_dim_v, v_in_k) = (256, 256, 0) with a
+ * group of 1..16 query heads per KV head (PR 37275: group 6 and 12 at head
+ * dim 256), and (576, 512, 1) with a group of 1..16 (PR 32779: 8 heads).
+ */
+typedef struct {
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim_qk;
+  int32_t head_dim_v;
+  int32_t topk;
+  int32_t v_in_k;
+  int32_t kv_dtype;  /* sa_dtype; only SA_DTYPE_BF16 is accepted */
+  float sm_scale;    /* multiplies q.k before the softmax */
+  int64_t q_row_stride;
+  int64_t kv_row_stride;
+  int64_t v_row_stride;
+  int64_t idx_row_stride;
+  int64_t out_row_stride;
+} sa_attn_desc;
+
+/* Per-token sparse prefill over one request
+ * (sglang PR 37275, "Motivation": each query row streams up to its top-k
+ * selected slots; PR 32779, "Motivation": one program per query token with
+ * the head group padded into a 16-row matrix tile, online softmax held in
+ * registers, no split partials).
+ *
+ * q, k, v, idx, out, lse  device pointers, layouts in sa_attn_desc
+ * topk_len  optional device int32 [num_rows]; slot j of row t is considered
+ *           only if j < topk_len[t] (PR 32779, "Robustness": the per-token
+ *           valid count); NULL = all topk slots
+ * num_rows  query rows (0 is allowed and launches nothing)
+ * kv_len    tokens in k/v; indices are valid in [0, kv_len)
+ * out, lse  fully written for every row and head.
+ */
+sa_status sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const void* k,
+                              const void* v, const int32_t* idx, const int32_t* topk_len,
+                              int32_t num_rows, int32_t kv_len, float* out, float* lse,
+                              hipStream_t stream);
+
+/* Ragged chunk prefill (sglang PR 37275, "Kernel measurements": the chunk
+ * kernel serves prefill with a cached prefix and every chunk after the
+ * first). Request r owns query rows [cu_seqlens_q[r], cu_seqlens_q[r+1]) and
+ * KV tokens [cu_seqlens_kv[r], cu_seqlens_kv[r+1]) of the packed k/v; its
+ * indices are local to that range.
+ *
+ * cu_seqlens_q   device int32 [num_reqs + 1], non-decreasing, [0] = 0,
+ *                [num_reqs] = total_q
+ * cu_seqlens_kv  device int64 [num_reqs + 1], non-decreasing, [0] = 0
+ * total_q        host copy of cu_seqlens_q[num_reqs] (sizes the grid, so no
+ *                device read is needed; PR 37275 "Not covered" notes the
+ *                device read its wrapper still did)
+ * The device arrays are trusted to be consistent with total_q.
+ */
+sa_status sparse_attn_chunk_prefill(const sa_attn_desc* desc, const void* q, const void* k,
+                                    const void* v, const int32_t* idx,
+                                    const int32_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                                    int32_t num_reqs, int32_t total_q, float* out, float* lse,
+                                    hipStream_t stream);
+
+/* Bytes of device workspace sparse_attn_union_build and
+ * sparse_attn_prefill_union need for these sizes (0 on invalid sizes). */
+size_t sparse_attn_union_workspace_bytes(int32_t num_rows, int32_t topk, int32_t G);
+
+/* Union-of-G index sets (sglang PR 32779, "Modifications",
+ * --dsa-triton-union): rows g*G .. g*G+G-1 form group g (the last group may
+ * be short). Each row's valid indices are sorted on their own; a row emits
+ * an index iff no earlier row of its group selected it; every row that
+ * selected it sets its ownership bit (bit j = j-th row of the group).
+ *
+ * idx         device int32 [num_rows][topk], row stride idx_row_stride
+ * union_idx   device int32 [ceil(num_rows/G)][G*topk]: row 0's distinct
+ *             valid indices ascending, then row 1's new ones ascending, ...;
+ *             -1 after union_len[g]
+ * union_bits  device uint8 [ceil(num_rows/G)][G*topk]; 0 after union_len[g]
+ * union_len   device int32 [ceil(num_rows/G)]
+ * ws          device workspace of sparse_attn_union_workspace_bytes bytes,
+ *             used only during the call
+ * G           1..8
+ * Output is bit-exact and deterministic.
+ */
+sa_status sparse_attn_union_build(const int32_t* idx, int64_t idx_row_stride, int32_t num_rows,
+                                  int32_t topk, int32_t kv_len, int32_t G, int32_t* union_idx,
+                                  uint8_t* union_bits, int32_t* union_len, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
+
+/* Union-mode sparse prefill (sglang PR 32779, "Modifications"): builds the
+ * union sets into ws, then one program per group gathers each union row
+ * once for all G * group query rows of the group; a row's scores are masked
+ * to -inf where its ownership bit is clear, so every row's result is that of
+ * the per-token path over its distinct valid indices.
+ * Legal iff G * group <= 32; otherwise the per-token path runs instead and
+ * SA_OK_FALLBACK is returned (PR 32779, review item 1).
+ * ws  device workspace of sparse_attn_union_workspace_bytes(num_rows, topk, G)
+ */
+sa_status sparse_attn_prefill_union(const sa_attn_desc* desc, const void* q, const void* k,
+                                    const void* v, const int32_t* idx, int32_t num_rows,
+                                    int32_t kv_len, int32_t G, void* ws, size_t ws_bytes,
+                                    float* out, float* lse, hipStream_t stream);
+
+/* Decode-pool page geometry (sglang PR 32320, "Modifications"). A source
+ * page holds src_page_tokens rows of row_bytes followed by src_page_tokens
+ * scales of scale_bytes; a destination page holds dst_page_tokens rows then
+ * their scales. src_page_tokens must be a multiple of dst_page_tokens. */
+typedef struct {
+  int32_t src_page_tokens;  /* 256 */
+  int32_t dst_page_tokens;  /* 64 */
+  int32_t row_bytes;        /* 656: one FP8 token row */
+  int32_t scale_bytes;      /* 4 */
+  int64_t src_page_stride;  /* bytes between source pages */
+  int64_t dst_page_stride;  /* bytes between destination pages */
+} sa_page_desc;
+
+/* Page mark (PR 32320, "_page_mark_kernel"): clears mask[0..num_src_pages)
+ * with a fill kernel, then sets mask[t / src_page_tokens] = 1 for every
+ * index t of idx[0..num_idx) with 0 <= t < num_src_pages * src_page_tokens.
+ * Other values (-1 padding, out-of-pool ids) are skipped. Same-value
+ * concurrent stores, no atomics; fixed grid, no host read.
+ * idx   device int32 [num_idx]
+ * mask  device int8 [num_src_pages], caller-owned and reusable
+ */
+sa_status page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src_pages,
+                    int32_t src_page_tokens, int8_t* mask, hipStream_t stream);
+
+/* Page split (PR 32320, "_page_split_kernel" with HAS_MASK): destination
+ * page p*ratio + s (ratio = src_page_tokens / dst_page_tokens) receives rows
+ * [s*dst_page_tokens, (s+1)*dst_page_tokens) of source page p and their
+ * scales. With a mask, source pages whose mask byte is 0 are skipped and
+ * their destination pages keep their previous bytes; NULL mask splits every
+ * page. Destination bytes past the scales of a page are never written.
+ * src   device uint8, num_src_pages pages at src_page_stride
+ * dst   device uint8, num_src_pages*ratio pages at dst_page_stride
+ */
+sa_status page_split(const sa_page_desc* desc, const uint8_t* src, uint8_t* dst,
+                     const int8_t* mask, int32_t num_src_pages, hipStream_t stream);
+
+/* Host-only check of an attention descriptor, as sparse_attn_prefill (G=1)
+ * or sparse_attn_prefill_union (G>1) would do before launching. Touches no
+ * device. Returns SA_OK, SA_OK_FALLBACK (union tile illegal) or an error. */
+int sa_validate_attn(const sa_attn_desc* desc, int32_t G);
+
+/* Message for the calling thread's last error ("" if none). */
+const char* sa_last_error(void);
+
+/* Number of successful calls per entry point since load, to rule out silent
+ * no-ops (PR 32779, "Speed Tests": invocations were counted). */
+typedef enum {
+  SA_ENTRY_PREFILL = 0,
+  SA_ENTRY_CHUNK_PREFILL = 1,
+  SA_ENTRY_UNION_BUILD = 2,
+  SA_ENTRY_PREFILL_UNION = 3,
+  SA_ENTRY_PAGE_MARK = 4,
+  SA_ENTRY_PAGE_SPLIT = 5,
+  SA_ENTRY_COUNT = 6
+} sa_entry;
+uint64_t sa_call_count(int32_t entry);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

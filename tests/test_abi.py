@@ -1,0 +1,130 @@
+"""The C-ABI library: loads without a GPU, exports every symbol the header
+declares, and its host-side validation returns the documented status codes
+(no device is touched by any call here)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import top_index_sparse_amd as sa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "sparse_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("sparse_attn_prefill", "sparse_attn_chunk_prefill", "sparse_attn_prefill_union",
+                 "sparse_attn_union_build", "sparse_attn_union_workspace_bytes", "page_mark",
+                 "page_split", "sa_validate_attn", "sa_last_error", "sa_call_count"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    handle = ctypes.CDLL(sa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(handle, name), name
+    assert sa.lib() is not None
+
+
+def _desc(**kw):
+    d = dict(num_q_heads=6, num_kv_heads=1, head_dim_qk=256, head_dim_v=256, topk=2051,
+             v_in_k=0, kv_dtype=sa.SA_DTYPE_BF16, sm_scale=1 / 16, q_row_stride=6 * 256,
+             kv_row_stride=256, v_row_stride=256, idx_row_stride=2051, out_row_stride=6 * 256)
+    d.update(kw)
+    return sa.AttnDesc(**d)
+
+
+def _mla(**kw):
+    d = dict(num_q_heads=8, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, topk=2048,
+             v_in_k=1, q_row_stride=8 * 576, kv_row_stride=576, v_row_stride=576,
+             idx_row_stride=2048, out_row_stride=8 * 512)
+    d.update(kw)
+    return _desc(**d)
+
+
+def test_validate_ok_shapes():
+    assert sa.sa_validate_attn(_desc()) == sa.SA_OK
+    assert sa.sa_validate_attn(_desc(num_q_heads=24, num_kv_heads=2, q_row_stride=24 * 256,
+                                     kv_row_stride=512, v_row_stride=512,
+                                     out_row_stride=24 * 256)) == sa.SA_OK
+    assert sa.sa_validate_attn(_mla()) == sa.SA_OK
+    assert sa.sa_validate_attn(_mla(), 2) == sa.SA_OK
+    assert sa.sa_validate_attn(_mla(), 4) == sa.SA_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv_dtype=sa.SA_DTYPE_FP8_E4M3), -3),
+    (dict(num_q_heads=7), -2),
+    (dict(num_q_heads=0), -2),
+    (dict(topk=0), -2),
+    (dict(sm_scale=math.inf), -2),
+    (dict(head_dim_qk=128, head_dim_v=128, q_row_stride=768, kv_row_stride=128,
+          v_row_stride=128, out_row_stride=768), -4),
+    (dict(num_q_heads=17, q_row_stride=17 * 256, out_row_stride=17 * 256), -4),
+    (dict(q_row_stride=6 * 256 - 8), -2),
+    (dict(q_row_stride=6 * 256 + 4), -2),
+    (dict(kv_row_stride=250), -2),
+    (dict(v_row_stride=260), -2),
+    (dict(idx_row_stride=2050), -2),
+    (dict(out_row_stride=6 * 256 + 2), -2),
+])
+def test_validate_rejects(kw, code):
+    assert sa.sa_validate_attn(_desc(**kw)) == code
+    assert sa.sa_last_error() != ""
+
+
+def test_union_fallback_and_g_range():
+    # 16 heads with G = 4 needs a 64-row tile: per-token fallback
+    d = _mla(num_q_heads=16, q_row_stride=16 * 576, out_row_stride=16 * 512)
+    assert sa.sa_validate_attn(d, 4) == sa.SA_OK_FALLBACK
+    assert sa.sa_validate_attn(d, 2) == sa.SA_OK
+    assert sa.sa_validate_attn(_mla(), 9) == -2
+    assert sa.sa_validate_attn(_mla(), 0) == -2
+
+
+def test_entry_points_reject_without_touching_device():
+    lib = sa.lib()
+    d = _desc()
+    # NULL pointers with rows > 0
+    st = lib.sparse_attn_prefill(ctypes.byref(d), None, None, None, None, None, 4, 10, None,
+                                 None, None)
+    assert st == -1
+    # misaligned q
+    st = lib.sparse_attn_prefill(ctypes.byref(d), 0x1008, 0x2000, 0x3000, 0x4000, None, 4, 10,
+                                 0x5000, 0x6000, None)
+    assert st == -2
+    # zero rows: nothing to launch
+    before = sa.sa_call_count("sparse_attn_prefill")
+    st = lib.sparse_attn_prefill(ctypes.byref(d), None, None, None, None, None, 0, 10, None,
+                                 None, None)
+    assert st == 0 and sa.sa_call_count("sparse_attn_prefill") == before + 1
+    # negative sizes
+    st = lib.sparse_attn_prefill(ctypes.byref(d), None, None, None, None, None, -1, 10, None,
+                                 None, None)
+    assert st == -2
+    # chunk prefill: rows but no requests
+    st = lib.sparse_attn_chunk_prefill(ctypes.byref(d), None, None, None, None, None, None, 0,
+                                       5, None, None, None)
+    assert st == -2
+    st = lib.sparse_attn_chunk_prefill(ctypes.byref(d), 0x1000, 0x2000, 0x3000, 0x4000, None,
+                                       None, 2, 5, 0x5000, 0x6000, None)
+    assert st == -1
+    # null desc
+    assert lib.sparse_attn_prefill(None, None, None, None, None, None, 1, 1, None, None,
+                                   None) == -1
+
+
+def test_bad_entry_count_is_zero():
+    assert sa.sa_call_count(99) == 0
+    assert sa.sa_call_count(-1) == 0

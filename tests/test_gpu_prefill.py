@@ -1,0 +1,225 @@
+"""GPU parity: per-token sparse prefill and ragged chunk prefill through the
+C ABI against the fp64 oracle, element by element."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+import top_index_sparse_amd as sa
+from tests.gpu_util import (attn_to_dev, bf16_dev, check_close, config, i32_dev, i64_dev,
+                            sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_prefill(case, dev, rows=None, **kw):
+    out, lse = sa.sparse_attn_prefill(dev["q"], dev["k"], dev["v"], dev["idx"],
+                                      sm_scale=case.scale, kv_len=case.kv_len,
+                                      head_dim_v=case.head_dim_v, **kw)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _oracle(case, rows=None, idx=None, topk_len=None):
+    return oracle.sparse_attention(case.q, case.k, case.v, case.idx if idx is None else idx,
+                                   num_kv_heads=case.num_kv_heads, scale=case.scale,
+                                   kv_len=case.kv_len, head_dim_v=case.head_dim_v,
+                                   topk_len=topk_len, rows=rows)
+
+
+@pytest.mark.parametrize("name", ["C0a", "C0b"])
+def test_tiny_config_all_rows(name):
+    say(f"[prefill] {name}")
+    case = config(name)
+    dev = attn_to_dev(case)
+    out, lse = _run_prefill(case, dev)
+    ro, rl = _oracle(case)
+    e, el = check_close(out, lse, ro, rl, name)
+    say(f"  max abs err O {e:.2e}  LSE {el:.2e}")
+
+
+def _small(seed, T, kv, first, Hq, Hkv, topk, walk=True):
+    return gen.make_attn_case("small", seed=seed, num_rows=T, kv_len=kv, first_pos=first,
+                              num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=256,
+                              head_dim_v=256, topk=topk, walk=walk)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(6, 1), (12, 1), (24, 2), (1, 1), (16, 1), (9, 3), (4, 2)])
+def test_groups_and_ragged_tail_tile(Hq, Hkv):
+    # 2051 = 128 * 16 + 3 slots: a 3-slot tail tile; 37 rows: 4-row groups with a tail
+    say(f"[prefill] group {Hq // Hkv} x {Hkv} KV heads, topk 2051")
+    case = _small(11, 37, 3000, 2900, Hq, Hkv, 2051)
+    dev = attn_to_dev(case)
+    out, lse = _run_prefill(case, dev)
+    ro, rl = _oracle(case)
+    check_close(out, lse, ro, rl, f"group {Hq}/{Hkv}")
+
+
+def test_invalid_slots_anywhere():
+    say("[prefill] -1, out-of-range, duplicates, all-invalid row, single slot")
+    case = _small(12, 21, 700, 650, 6, 1, 100)
+    idx = case.idx.copy()
+    rng = np.random.default_rng(5)
+    holes = rng.random(idx.shape) < 0.3
+    idx[holes] = -1
+    idx[1, ::3] = 700                      # == kv_len: out of range
+    idx[2, ::5] = 10 ** 9
+    idx[3, ::7] = -(10 ** 9)
+    idx[4, :] = -1                         # empty support
+    idx[5, :] = -1
+    idx[5, 57] = 123                       # one valid slot
+    idx[6, 10:40] = idx[6, 9]              # duplicates count with multiplicity
+    idx[7, :95] = -1                       # only the tail tile is valid
+    case.idx = idx
+    dev = attn_to_dev(case)
+    out, lse = _run_prefill(case, dev)
+    ro, rl = _oracle(case)
+    check_close(out, lse, ro, rl, "invalid slots")
+    assert torch.all(out[4] == 0) and torch.all(torch.isneginf(lse[4]))
+
+
+def test_topk_len_hint():
+    say("[prefill] topk_len")
+    case = _small(13, 17, 900, 880, 6, 1, 300)
+    tl = np.random.default_rng(3).integers(-2, 320, size=17).astype(np.int32)
+    dev = attn_to_dev(case)
+    out, lse = _run_prefill(case, dev, topk_len=i32_dev(tl))
+    ro, rl = _oracle(case, topk_len=tl)
+    check_close(out, lse, ro, rl, "topk_len")
+
+
+def test_kv_len_smaller_than_buffer():
+    say("[prefill] kv_len < buffer rows")
+    case = _small(14, 9, 500, 480, 6, 1, 64, walk=False)
+    dev = attn_to_dev(case)
+    case.kv_len = 300
+    out, lse = _run_prefill(case, dev)
+    ro, rl = _oracle(case)
+    check_close(out, lse, ro, rl, "kv_len")
+
+
+def test_strided_rows_and_full_overwrite():
+    say("[prefill] padded row strides, NaN-poisoned outputs, guard bands")
+    case = _small(15, 13, 800, 780, 12, 1, 200)
+    q = bf16_dev(case.q)
+    k = bf16_dev(case.k)
+    v = bf16_dev(case.v)
+    qp = torch.zeros((13, 12 * 256 + 64), dtype=torch.bfloat16, device="cuda")
+    qp[:, :12 * 256] = q.reshape(13, -1)
+    qv = qp[:, :12 * 256].view(13, 12, 256)
+    kp = torch.zeros((800, 256 + 8), dtype=torch.bfloat16, device="cuda")
+    kp[:, :256] = k.reshape(800, 256)
+    vp = torch.zeros((800, 256 + 24), dtype=torch.bfloat16, device="cuda")
+    vp[:, :256] = v.reshape(800, 256)
+    ip = torch.full((13, 256), -7, dtype=torch.int32, device="cuda")
+    ip[:, :200] = i32_dev(case.idx)
+    guard = 4096
+    obuf = torch.full((guard * 2 + 13 * (12 * 256 + 4),), float("nan"), device="cuda")
+    out = obuf[guard:guard + 13 * (12 * 256 + 4)].view(13, 12 * 256 + 4)[:, :12 * 256].view(13, 12, 256)
+    lbuf = torch.full((guard * 2 + 13 * 12,), float("nan"), device="cuda")
+    lse = lbuf[guard:guard + 13 * 12].view(13, 12)
+    sa.sparse_attn_prefill(qv, kp[:, :256].view(800, 1, 256), vp[:, :256].view(800, 1, 256),
+                           ip[:, :200], sm_scale=case.scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = _oracle(case)
+    check_close(out, lse, ro, rl, "strided")
+    assert torch.isnan(obuf[:guard]).all() and torch.isnan(obuf[-guard:]).all()
+    pad = obuf[guard:guard + 13 * (12 * 256 + 4)].view(13, -1)[:, 12 * 256:]
+    assert torch.isnan(pad).all(), "row padding of out must not be written"
+    assert torch.isnan(lbuf[:guard]).all() and torch.isnan(lbuf[-guard:]).all()
+
+
+def test_side_stream_and_bitwise_replay():
+    say("[prefill] side stream + replay")
+    case = config("C0b")
+    dev = attn_to_dev(case)
+    o1, l1 = _run_prefill(case, dev)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = sa.sparse_attn_prefill(dev["q"], dev["k"], dev["v"], dev["idx"],
+                                        sm_scale=case.scale, stream=s)
+    s.synchronize()
+    o3, l3 = _run_prefill(case, dev)
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+    assert torch.equal(l1, l2) and torch.equal(l1, l3)
+
+
+def test_call_counter_counts():
+    case = config("C0a")
+    dev = attn_to_dev(case)
+    before = sa.sa_call_count("sparse_attn_prefill")
+    _run_prefill(case, dev)
+    assert sa.sa_call_count("sparse_attn_prefill") == before + 1
+
+
+@pytest.mark.parametrize("name,nrows", [("C1", 48), ("C2", 24)])
+def test_full_size_sampled(name, nrows):
+    say(f"[prefill] {name} full size, sampled rows")
+    case = config(name)
+    dev = attn_to_dev(case)
+    out, lse = _run_prefill(case, dev)
+    rows = sample_rows(case.num_rows, nrows)
+    ro, rl = _oracle(case, rows=rows)
+    e, el = check_close(out[torch.from_numpy(rows).cuda()], lse[torch.from_numpy(rows).cuda()],
+                        ro, rl, name)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    say(f"  {name}: max abs err O {e:.2e}  LSE {el:.2e} over {len(rows)} rows")
+
+
+def test_c1_through_chunk_prefill_equals_prefill():
+    say("[chunk] C1 as one request == prefill, bitwise")
+    case = config("C1")
+    dev = attn_to_dev(case)
+    o1, l1 = _run_prefill(case, dev)
+    cu_q = i32_dev(np.array([0, case.num_rows]))
+    cu_kv = i64_dev(np.array([0, case.kv_len]))
+    o2, l2 = sa.sparse_attn_chunk_prefill(dev["q"], dev["k"], dev["v"], dev["idx"], cu_q, cu_kv,
+                                          sm_scale=case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def _chunk(case, dev):
+    out, lse = sa.sparse_attn_chunk_prefill(dev["q"], dev["k"], dev["v"], dev["idx"],
+                                            dev["cu_q"], dev["cu_kv"], sm_scale=case.scale)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def test_chunk_prefill_small_ragged():
+    say("[chunk] small ragged batch with empty requests")
+    case = gen.make_ragged_case("r", seed=21, num_reqs=6, qlen_range=(1, 40),
+                                ctx_range=(100, 600), num_q_heads=6, num_kv_heads=1,
+                                head_dim=256, topk=130)
+    # make requests 1 and 4 empty
+    qlens = np.diff(case.cu_seqlens_q)
+    keep = np.ones(case.num_rows, bool)
+    keep[case.cu_seqlens_q[1]:case.cu_seqlens_q[2]] = False
+    keep[case.cu_seqlens_q[4]:case.cu_seqlens_q[5]] = False
+    qlens[[1, 4]] = 0
+    case.q, case.idx, case.positions = case.q[keep], case.idx[keep], case.positions[keep]
+    case.cu_seqlens_q = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    dev = attn_to_dev(case)
+    out, lse = _chunk(case, dev)
+    ro, rl = oracle.chunk_prefill(case.q, case.k, case.v, case.idx, case.cu_seqlens_q,
+                                  case.cu_seqlens_kv, num_kv_heads=1, scale=case.scale)
+    check_close(out, lse, ro, rl, "ragged small")
+
+
+def test_chunk_prefill_c4_sampled():
+    say("[chunk] C4 full size, sampled rows")
+    case = config("C4")
+    dev = attn_to_dev(case)
+    out, lse = _chunk(case, dev)
+    rows = sample_rows(case.num_rows, 48)
+    # include each request's first and last row
+    rows = np.unique(np.concatenate([rows, case.cu_seqlens_q[:-1], case.cu_seqlens_q[1:] - 1]))
+    ro, rl = oracle.chunk_prefill(case.q, case.k, case.v, case.idx, case.cu_seqlens_q,
+                                  case.cu_seqlens_kv, num_kv_heads=1, scale=case.scale, rows=rows)
+    sel = torch.from_numpy(rows).cuda()
+    e, el = check_close(out[sel], lse[sel], ro, rl, "C4")
+    assert torch.isfinite(out).all()
+    say(f"  C4: max abs err O {e:.2e}  LSE {el:.2e} over {len(rows)} rows")

@@ -1,0 +1,235 @@
+// C ABI of the sparse attention library: argument validation, launch
+// geometry, status codes, per-thread error text and call counters.
+// Nothing here allocates device memory or reads it back.
+#include "sparse_attn.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "sa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+std::atomic<uint64_t> g_calls[SA_ENTRY_COUNT];
+
+sa_status fail(sa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+sa_status ok(sa_entry e, sa_status st = SA_OK) {
+  g_calls[e].fetch_add(1, std::memory_order_relaxed);
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+enum class Kernel { kNone, kGqa256, kMla576 };
+
+// Which built kernel serves this descriptor (no pointer checks).
+sa_status check_desc(const sa_attn_desc* d, int32_t G, Kernel* kernel) {
+  if (!d) return fail(SA_ERR_NULL, "desc is NULL");
+  if (d->kv_dtype != SA_DTYPE_BF16)
+    return fail(SA_ERR_DTYPE, "kv_dtype %d: only bf16 K/V is accepted", d->kv_dtype);
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads != 0)
+    return fail(SA_ERR_SHAPE, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                d->num_q_heads, d->num_kv_heads);
+  if (d->topk <= 0) return fail(SA_ERR_SHAPE, "topk %d must be positive", d->topk);
+  if (!std::isfinite(d->sm_scale)) return fail(SA_ERR_SHAPE, "sm_scale is not finite");
+  if (d->head_dim_qk <= 0 || d->head_dim_v <= 0)
+    return fail(SA_ERR_SHAPE, "head dims must be positive");
+  if (d->v_in_k && d->head_dim_v > d->head_dim_qk)
+    return fail(SA_ERR_SHAPE, "v_in_k needs head_dim_v <= head_dim_qk");
+  const int group = d->num_q_heads / d->num_kv_heads;
+  if (d->head_dim_qk == 256 && d->head_dim_v == 256 && !d->v_in_k) {
+    *kernel = Kernel::kGqa256;
+  } else if (d->head_dim_qk == 576 && d->head_dim_v == 512 && d->v_in_k) {
+    *kernel = Kernel::kMla576;
+  } else {
+    return fail(SA_ERR_UNSUPPORTED,
+                "head dims (%d, %d, v_in_k=%d) not built; built: (256, 256, 0), (576, 512, 1)",
+                d->head_dim_qk, d->head_dim_v, d->v_in_k);
+  }
+  if (group > 16) return fail(SA_ERR_UNSUPPORTED, "group %d > 16 query heads per KV head", group);
+  const int64_t qrow = (int64_t)d->num_q_heads * d->head_dim_qk;
+  const int64_t krow = (int64_t)d->num_kv_heads * d->head_dim_qk;
+  const int64_t vrow = (int64_t)d->num_kv_heads * d->head_dim_v;
+  const int64_t orow = (int64_t)d->num_q_heads * d->head_dim_v;
+  if (d->q_row_stride < qrow || d->q_row_stride % 8)
+    return fail(SA_ERR_SHAPE, "q_row_stride %lld: needs >= %lld and a multiple of 8",
+                (long long)d->q_row_stride, (long long)qrow);
+  if (d->kv_row_stride < krow || d->kv_row_stride % 8)
+    return fail(SA_ERR_SHAPE, "kv_row_stride %lld: needs >= %lld and a multiple of 8",
+                (long long)d->kv_row_stride, (long long)krow);
+  if (!d->v_in_k && (d->v_row_stride < vrow || d->v_row_stride % 8))
+    return fail(SA_ERR_SHAPE, "v_row_stride %lld: needs >= %lld and a multiple of 8",
+                (long long)d->v_row_stride, (long long)vrow);
+  if (d->idx_row_stride < d->topk)
+    return fail(SA_ERR_SHAPE, "idx_row_stride %lld < topk %d", (long long)d->idx_row_stride,
+                d->topk);
+  if (d->out_row_stride < orow || d->out_row_stride % 4)
+    return fail(SA_ERR_SHAPE, "out_row_stride %lld: needs >= %lld and a multiple of 4",
+                (long long)d->out_row_stride, (long long)orow);
+  if (G < 1 || G > 8) return fail(SA_ERR_SHAPE, "union group size G %d outside 1..8", G);
+  if (G > 1 && G * group > 32) return SA_OK_FALLBACK;
+  return SA_OK;
+}
+
+sa_status check_ptrs(const sa_attn_desc* d, const void* q, const void* k, const void* v,
+                     const int32_t* idx, const float* out, const float* lse) {
+  if (!q || !k || !idx || !out || !lse || (!d->v_in_k && !v))
+    return fail(SA_ERR_NULL, "q, k, v (unless v_in_k), idx, out and lse are required");
+  if (!aligned16(q) || !aligned16(k) || (!d->v_in_k && !aligned16(v)) || !aligned16(out))
+    return fail(SA_ERR_SHAPE, "q, k, v and out must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(idx) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(SA_ERR_SHAPE, "idx and lse must be 4-byte aligned");
+  return SA_OK;
+}
+
+sa::AttnParams make_params(const sa_attn_desc* d, const void* q, const void* k, const void* v,
+                           const int32_t* idx, float* out, float* lse, int32_t num_rows) {
+  sa::AttnParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = d->v_in_k ? p.k : static_cast<const uint16_t*>(v);
+  p.idx = idx;
+  p.out = out;
+  p.lse = lse;
+  p.q_row_stride = d->q_row_stride;
+  p.k_row_stride = d->kv_row_stride;
+  p.v_row_stride = d->v_in_k ? d->kv_row_stride : d->v_row_stride;
+  p.idx_row_stride = d->idx_row_stride;
+  p.out_row_stride = d->out_row_stride;
+  p.num_rows = num_rows;
+  p.topk = d->topk;
+  p.num_q_heads = d->num_q_heads;
+  p.num_kv_heads = d->num_kv_heads;
+  p.group = d->num_q_heads / d->num_kv_heads;
+  p.scale_log2e = d->sm_scale * 1.4426950408889634f;
+  return p;
+}
+
+sa_status launch_attention(Kernel kernel, const sa::AttnParams& p, bool ragged, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  switch (kernel) {
+    case Kernel::kGqa256:
+      e = sa::launch_gqa_d256(p, ragged, s);
+      break;
+    default:
+      return fail(SA_ERR_UNSUPPORTED, "this head-dim combination has no kernel yet");
+  }
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sa_validate_attn(const sa_attn_desc* desc, int32_t G) {
+  Kernel kernel = Kernel::kNone;
+  return check_desc(desc, G, &kernel);
+}
+
+const char* sa_last_error(void) { return g_err; }
+
+uint64_t sa_call_count(int32_t entry) {
+  if (entry < 0 || entry >= SA_ENTRY_COUNT) return 0;
+  return g_calls[entry].load(std::memory_order_relaxed);
+}
+
+sa_status sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const void* k,
+                              const void* v, const int32_t* idx, const int32_t* topk_len,
+                              int32_t num_rows, int32_t kv_len, float* out, float* lse,
+                              hipStream_t stream) {
+  g_err[0] = 0;
+  Kernel kernel = Kernel::kNone;
+  sa_status st = check_desc(desc, 1, &kernel);
+  if (st != SA_OK) return st;
+  if (num_rows < 0 || kv_len < 0)
+    return fail(SA_ERR_SHAPE, "num_rows %d and kv_len %d must be >= 0", num_rows, kv_len);
+  if (num_rows == 0) return ok(SA_ENTRY_PREFILL);
+  st = check_ptrs(desc, q, k, v, idx, out, lse);
+  if (st != SA_OK) return st;
+  if ((int64_t)(num_rows + 3) / 4 * desc->num_kv_heads > INT32_MAX)
+    return fail(SA_ERR_SHAPE, "too many rows for one launch");
+  sa::AttnParams p = make_params(desc, q, k, v, idx, out, lse, num_rows);
+  p.topk_len = topk_len;
+  p.kv_len = kv_len;
+  p.num_reqs = 1;
+  st = launch_attention(kernel, p, false, stream);
+  return st == SA_OK ? ok(SA_ENTRY_PREFILL) : st;
+}
+
+sa_status sparse_attn_chunk_prefill(const sa_attn_desc* desc, const void* q, const void* k,
+                                    const void* v, const int32_t* idx,
+                                    const int32_t* cu_seqlens_q, const int64_t* cu_seqlens_kv,
+                                    int32_t num_reqs, int32_t total_q, float* out, float* lse,
+                                    hipStream_t stream) {
+  g_err[0] = 0;
+  Kernel kernel = Kernel::kNone;
+  sa_status st = check_desc(desc, 1, &kernel);
+  if (st != SA_OK) return st;
+  if (num_reqs < 0 || total_q < 0)
+    return fail(SA_ERR_SHAPE, "num_reqs %d and total_q %d must be >= 0", num_reqs, total_q);
+  if (total_q == 0 || num_reqs == 0) {
+    if (total_q != 0) return fail(SA_ERR_SHAPE, "total_q %d rows but no request", total_q);
+    return ok(SA_ENTRY_CHUNK_PREFILL);
+  }
+  if (!cu_seqlens_q || !cu_seqlens_kv) return fail(SA_ERR_NULL, "cu_seqlens_q/kv are required");
+  st = check_ptrs(desc, q, k, v, idx, out, lse);
+  if (st != SA_OK) return st;
+  sa::AttnParams p = make_params(desc, q, k, v, idx, out, lse, total_q);
+  p.cu_q = cu_seqlens_q;
+  p.cu_kv = cu_seqlens_kv;
+  p.num_reqs = num_reqs;
+  st = launch_attention(kernel, p, true, stream);
+  return st == SA_OK ? ok(SA_ENTRY_CHUNK_PREFILL) : st;
+}
+
+size_t sparse_attn_union_workspace_bytes(int32_t num_rows, int32_t topk, int32_t G) {
+  (void)num_rows;
+  (void)topk;
+  (void)G;
+  return 0;
+}
+
+sa_status sparse_attn_union_build(const int32_t* idx, int64_t idx_row_stride, int32_t num_rows,
+                                  int32_t topk, int32_t kv_len, int32_t G, int32_t* union_idx,
+                                  uint8_t* union_bits, int32_t* union_len, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  (void)idx; (void)idx_row_stride; (void)num_rows; (void)topk; (void)kv_len; (void)G;
+  (void)union_idx; (void)union_bits; (void)union_len; (void)ws; (void)ws_bytes; (void)stream;
+  return fail(SA_ERR_UNSUPPORTED, "union build not built yet");
+}
+
+sa_status sparse_attn_prefill_union(const sa_attn_desc* desc, const void* q, const void* k,
+                                    const void* v, const int32_t* idx, int32_t num_rows,
+                                    int32_t kv_len, int32_t G, void* ws, size_t ws_bytes,
+                                    float* out, float* lse, hipStream_t stream) {
+  (void)desc; (void)q; (void)k; (void)v; (void)idx; (void)num_rows; (void)kv_len; (void)G;
+  (void)ws; (void)ws_bytes; (void)out; (void)lse; (void)stream;
+  return fail(SA_ERR_UNSUPPORTED, "union prefill not built yet");
+}
+
+sa_status page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src_pages,
+                    int32_t src_page_tokens, int8_t* mask, hipStream_t stream) {
+  (void)idx; (void)num_idx; (void)num_src_pages; (void)src_page_tokens; (void)mask;
+  (void)stream;
+  return fail(SA_ERR_UNSUPPORTED, "page_mark not built yet");
+}
+
+sa_status page_split(const sa_page_desc* desc, const uint8_t* src, uint8_t* dst,
+                     const int8_t* mask, int32_t num_src_pages, hipStream_t stream) {
+  (void)desc; (void)src; (void)dst; (void)mask; (void)num_src_pages; (void)stream;
+  return fail(SA_ERR_UNSUPPORTED, "page_split not built yet");
+}
+
+}  // extern "C"

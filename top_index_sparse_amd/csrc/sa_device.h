@@ -1,0 +1,81 @@
+// Device helpers shared by the gfx950 kernels: vector types, 16-byte loads,
+// bf16 packing, MFMA wrappers, XCD-aware block remapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+__device__ __forceinline__ void st16(void* p, f32x4_t v) {
+  *reinterpret_cast<f32x4_t*>(p) = v;
+}
+
+// Two fp32 values to packed bf16 (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t h = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// bf16 element e (0..7) of a 16-byte chunk.
+__device__ __forceinline__ uint32_t bf16_elem(u32x4_t v, int e) {
+  const uint32_t w = v[e >> 1];
+  return (e & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// Pack element e of four chunks into the 4 x bf16 operand of a K=16 MFMA.
+__device__ __forceinline__ i16x4_t gather_col4(u32x4_t c0, u32x4_t c1, u32x4_t c2, u32x4_t c3,
+                                               int e) {
+  const uint32_t w0 = c0[e >> 1], w1 = c1[e >> 1], w2 = c2[e >> 1], w3 = c3[e >> 1];
+  uint32_t lo, hi;
+  if (e & 1) {
+    lo = (w0 >> 16) | (w1 & 0xffff0000u);
+    hi = (w2 >> 16) | (w3 & 0xffff0000u);
+  } else {
+    lo = (w0 & 0xffffu) | (w1 << 16);
+    hi = (w2 & 0xffffu) | (w3 << 16);
+  }
+  return __builtin_bit_cast(i16x4_t, (u32x2_t){lo, hi});
+}
+
+// D = A(16x32) * B(32x16) + C; lane l holds A row l%16, B column l%16, each
+// with k = 8*(l/16) .. 8*(l/16)+7; C/D lane l holds column l%16, rows
+// 4*(l/16) .. 4*(l/16)+3.
+__device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// D = A(16x16) * B(16x16) + C with k = 4*(l/16) .. 4*(l/16)+3 per lane.
+__device__ __forceinline__ f32x4_t mfma_16x16x16(i16x4_t a, i16x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).
+// Remap so that XCD x runs a contiguous band of logical block ids, keeping
+// neighbouring rows (which share most of their indices) in one L2.
+__device__ __forceinline__ int xcd_remap(int b, int nblk) {
+  constexpr int X = 8;
+  const int q = nblk / X, r = nblk % X;
+  const int xcd = b % X, local = b / X;
+  return xcd * q + (xcd < r ? xcd : r) + local;
+}
+
+}  // namespace sa

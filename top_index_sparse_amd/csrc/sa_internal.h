@@ -1,0 +1,74 @@
+// Internal interface between the C ABI (sa_api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+// One attention launch. Pointers are device pointers; strides in elements.
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;          // == k when V lives in the K row
+  const int32_t* idx;
+  const int32_t* topk_len;    // nullable
+  const int32_t* cu_q;        // ragged only
+  const int64_t* cu_kv;       // ragged only
+  float* out;
+  float* lse;
+  int64_t q_row_stride;
+  int64_t k_row_stride;
+  int64_t v_row_stride;
+  int64_t idx_row_stride;
+  int64_t out_row_stride;
+  int32_t num_rows;
+  int32_t num_reqs;
+  int32_t kv_len;             // non-ragged KV length
+  int32_t topk;
+  int32_t group;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  float scale_log2e;          // sm_scale * log2(e)
+};
+
+// Union attention over prebuilt union sets.
+struct UnionAttnParams {
+  AttnParams a;               // q, k, v, out, lse, strides, heads, scale
+  const int32_t* union_idx;   // [groups][union_stride]
+  const uint8_t* union_bits;  // [groups][union_stride]
+  const int32_t* union_len;   // [groups]
+  int64_t union_stride;       // G * topk
+  int32_t G;
+};
+
+struct UnionBuildParams {
+  const int32_t* idx;
+  int64_t idx_row_stride;
+  int32_t num_rows;
+  int32_t topk;
+  int32_t kv_len;
+  int32_t G;
+  int32_t* sorted;            // workspace [num_rows][topk_pad]
+  int32_t topk_pad;
+  int32_t* union_idx;
+  uint8_t* union_bits;
+  int32_t* union_len;
+};
+
+struct PageParams {
+  const uint8_t* src;
+  uint8_t* dst;
+  const int8_t* mask;         // nullable
+  int64_t src_page_stride;
+  int64_t dst_page_stride;
+  int32_t num_src_pages;
+  int32_t src_page_tokens;
+  int32_t dst_page_tokens;
+  int32_t row_bytes;
+  int32_t scale_bytes;
+};
+
+hipError_t launch_gqa_d256(const AttnParams& p, bool ragged, hipStream_t stream);
+
+}  // namespace sa
