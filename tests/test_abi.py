@@ -128,3 +128,50 @@ def test_entry_points_reject_without_touching_device():
 def test_bad_entry_count_is_zero():
     assert sa.sa_call_count(99) == 0
     assert sa.sa_call_count(-1) == 0
+
+
+def test_union_workspace_bytes():
+    n = sa.sparse_attn_union_workspace_bytes(4096, 2048, 4)
+    # sorted keys + union rows (int32 + uint8) + lengths
+    assert n >= 4096 * 2048 * 4 + 1024 * 8192 * 5 + 1024 * 4
+    assert n % 256 == 0
+    assert sa.sparse_attn_union_workspace_bytes(10, 2051, 2) >= 10 * 4096 * 4
+    assert sa.sparse_attn_union_workspace_bytes(10, 0, 2) == 0
+    assert sa.sparse_attn_union_workspace_bytes(10, 20, 9) == 0
+    assert sa.sparse_attn_union_workspace_bytes(10, 9000, 2) == 0
+    assert sa.sparse_attn_union_workspace_bytes(-1, 20, 2) == 0
+
+
+def test_union_build_and_pages_reject_on_host():
+    lib = sa.lib()
+    # bad G, missing workspace, null outputs
+    assert lib.sparse_attn_union_build(0x1000, 8, 4, 8, 100, 9, 0x2000, 0x3000, 0x4000, 0x5000,
+                                       1 << 20, None) == -2
+    assert lib.sparse_attn_union_build(0x1000, 8, 4, 8, 100, 2, 0x2000, 0x3000, 0x4000, None, 0,
+                                       None) == -5
+    assert lib.sparse_attn_union_build(0x1000, 8, 4, 8, 100, 2, None, 0x3000, 0x4000, 0x5000,
+                                       1 << 20, None) == -1
+    assert lib.sparse_attn_union_build(0x1000, 4, 4, 8, 100, 2, 0x2000, 0x3000, 0x4000, 0x5000,
+                                       1 << 20, None) == -2
+    d = sa.PageDesc(src_page_tokens=256, dst_page_tokens=96, row_bytes=656, scale_bytes=4,
+                    src_page_stride=168960, dst_page_stride=42240)
+    assert lib.page_split(ctypes.byref(d), 0x1000, 0x2000, None, 4, None) == -2
+    d = sa.PageDesc(src_page_tokens=256, dst_page_tokens=64, row_bytes=656, scale_bytes=4,
+                    src_page_stride=168960, dst_page_stride=42000)
+    assert lib.page_split(ctypes.byref(d), 0x1000, 0x2000, None, 4, None) == -2
+    d.dst_page_stride = 42240
+    assert lib.page_split(ctypes.byref(d), None, 0x2000, None, 4, None) == -1
+    assert lib.page_split(None, None, None, None, 4, None) == -1
+    assert lib.page_mark(0x1000, 10, 4096, 0, 0x2000, None) == -2
+    assert lib.page_mark(0x1000, 10, 4096, 256, None, None) == -1
+    assert lib.page_mark(None, 10, 4096, 256, 0x2000, None) == -1
+
+
+def test_prefill_union_rejects_on_host():
+    lib = sa.lib()
+    d = _mla()
+    # workspace too small for a legal union
+    st = lib.sparse_attn_prefill_union(ctypes.byref(d), 0x1000, 0x2000, None, 0x3000, 8, 100, 2,
+                                       None, 0, 0x4000, 0x5000, None)
+    assert st == -5
+    assert "workspace" in sa.sa_last_error()

@@ -116,17 +116,65 @@ sa::AttnParams make_params(const sa_attn_desc* d, const void* q, const void* k, 
   return p;
 }
 
-sa_status launch_attention(Kernel kernel, const sa::AttnParams& p, bool ragged, hipStream_t s) {
+sa_status launch_attention(Kernel kernel, const sa::AttnParams& p, int mode, hipStream_t s) {
   hipError_t e = hipSuccess;
   switch (kernel) {
     case Kernel::kGqa256:
-      e = sa::launch_gqa_d256(p, ragged, s);
+      e = sa::launch_attn_gqa256(p, mode, s);
+      break;
+    case Kernel::kMla576:
+      e = sa::launch_attn_mla576(p, mode, s);
       break;
     default:
-      return fail(SA_ERR_UNSUPPORTED, "this head-dim combination has no kernel yet");
+      return fail(SA_ERR_UNSUPPORTED, "no kernel for this head-dim combination");
   }
   if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return SA_OK;
+}
+
+constexpr int kMaxTopkPad = 8192;  // sort keys held in 32 KB of LDS
+
+int64_t pow2_at_least(int64_t x) {
+  int64_t p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Workspace layout shared by union_build and prefill_union.
+struct UnionLayout {
+  int64_t topk_pad, groups, stride;
+  int64_t sorted_off, idx_off, bits_off, len_off, total;
+};
+
+bool union_layout(int32_t num_rows, int32_t topk, int32_t G, UnionLayout* L) {
+  if (num_rows < 0 || topk <= 0 || G < 1 || G > 8) return false;
+  L->topk_pad = pow2_at_least(topk < 2 ? 2 : topk);
+  if (L->topk_pad > kMaxTopkPad) return false;
+  L->groups = (num_rows + G - 1) / G;
+  L->stride = align_up((int64_t)G * topk, 16);
+  L->sorted_off = 0;
+  L->idx_off = align_up((int64_t)num_rows * L->topk_pad * 4, 256);
+  L->bits_off = L->idx_off + align_up(L->groups * L->stride * 4, 256);
+  L->len_off = L->bits_off + align_up(L->groups * L->stride, 256);
+  L->total = L->len_off + align_up(L->groups * 4, 256);
+  return true;
+}
+
+sa::UnionBuildParams build_params(const int32_t* idx, int64_t idx_row_stride, int32_t num_rows,
+                                  int32_t topk, int32_t kv_len, int32_t G, const UnionLayout& L,
+                                  void* ws) {
+  sa::UnionBuildParams b{};
+  b.idx = idx;
+  b.idx_row_stride = idx_row_stride;
+  b.num_rows = num_rows;
+  b.topk = topk;
+  b.kv_len = kv_len;
+  b.G = G;
+  b.sorted = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + L.sorted_off);
+  b.topk_pad = (int32_t)L.topk_pad;
+  return b;
 }
 
 }  // namespace
@@ -164,7 +212,7 @@ sa_status sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const voi
   p.topk_len = topk_len;
   p.kv_len = kv_len;
   p.num_reqs = 1;
-  st = launch_attention(kernel, p, false, stream);
+  st = launch_attention(kernel, p, 0, stream);
   return st == SA_OK ? ok(SA_ENTRY_PREFILL) : st;
 }
 
@@ -190,46 +238,143 @@ sa_status sparse_attn_chunk_prefill(const sa_attn_desc* desc, const void* q, con
   p.cu_q = cu_seqlens_q;
   p.cu_kv = cu_seqlens_kv;
   p.num_reqs = num_reqs;
-  st = launch_attention(kernel, p, true, stream);
+  st = launch_attention(kernel, p, 1, stream);
   return st == SA_OK ? ok(SA_ENTRY_CHUNK_PREFILL) : st;
 }
 
 size_t sparse_attn_union_workspace_bytes(int32_t num_rows, int32_t topk, int32_t G) {
-  (void)num_rows;
-  (void)topk;
-  (void)G;
-  return 0;
+  UnionLayout L;
+  if (!union_layout(num_rows, topk, G, &L)) return 0;
+  return (size_t)L.total;
 }
 
 sa_status sparse_attn_union_build(const int32_t* idx, int64_t idx_row_stride, int32_t num_rows,
                                   int32_t topk, int32_t kv_len, int32_t G, int32_t* union_idx,
                                   uint8_t* union_bits, int32_t* union_len, void* ws,
                                   size_t ws_bytes, hipStream_t stream) {
-  (void)idx; (void)idx_row_stride; (void)num_rows; (void)topk; (void)kv_len; (void)G;
-  (void)union_idx; (void)union_bits; (void)union_len; (void)ws; (void)ws_bytes; (void)stream;
-  return fail(SA_ERR_UNSUPPORTED, "union build not built yet");
+  g_err[0] = 0;
+  UnionLayout L;
+  if (num_rows < 0 || kv_len < 0 || !union_layout(num_rows, topk, G, &L))
+    return fail(SA_ERR_SHAPE, "num_rows %d, topk %d (<= %d), G %d (1..8), kv_len %d", num_rows,
+                topk, kMaxTopkPad, G, kv_len);
+  if (idx_row_stride < topk) return fail(SA_ERR_SHAPE, "idx_row_stride < topk");
+  if (num_rows == 0) return ok(SA_ENTRY_UNION_BUILD);
+  if (!idx || !union_idx || !union_bits || !union_len)
+    return fail(SA_ERR_NULL, "idx and the three outputs are required");
+  if (!ws || ws_bytes < (size_t)L.idx_off)
+    return fail(SA_ERR_WORKSPACE, "workspace of %zu bytes, %lld needed", ws_bytes,
+                (long long)L.idx_off);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) || (reinterpret_cast<uintptr_t>(idx) & 3) ||
+      (reinterpret_cast<uintptr_t>(union_idx) & 3) || (reinterpret_cast<uintptr_t>(union_len) & 3))
+    return fail(SA_ERR_SHAPE, "ws must be 256-byte aligned; idx and int32 outputs 4-byte aligned");
+  sa::UnionBuildParams b = build_params(idx, idx_row_stride, num_rows, topk, kv_len, G, L, ws);
+  b.union_idx = union_idx;
+  b.union_bits = union_bits;
+  b.union_len = union_len;
+  b.union_stride = (int64_t)G * topk;
+  const hipError_t e = sa::launch_union_build(b, stream);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok(SA_ENTRY_UNION_BUILD);
 }
 
 sa_status sparse_attn_prefill_union(const sa_attn_desc* desc, const void* q, const void* k,
                                     const void* v, const int32_t* idx, int32_t num_rows,
                                     int32_t kv_len, int32_t G, void* ws, size_t ws_bytes,
                                     float* out, float* lse, hipStream_t stream) {
-  (void)desc; (void)q; (void)k; (void)v; (void)idx; (void)num_rows; (void)kv_len; (void)G;
-  (void)ws; (void)ws_bytes; (void)out; (void)lse; (void)stream;
-  return fail(SA_ERR_UNSUPPORTED, "union prefill not built yet");
+  g_err[0] = 0;
+  Kernel kernel = Kernel::kNone;
+  const sa_status legal = check_desc(desc, G, &kernel);
+  if (legal != SA_OK && legal != SA_OK_FALLBACK) return legal;
+  if (num_rows < 0 || kv_len < 0)
+    return fail(SA_ERR_SHAPE, "num_rows %d and kv_len %d must be >= 0", num_rows, kv_len);
+  if (num_rows == 0) return ok(SA_ENTRY_PREFILL_UNION, legal);
+  sa_status st = check_ptrs(desc, q, k, v, idx, out, lse);
+  if (st != SA_OK) return st;
+  sa::AttnParams p = make_params(desc, q, k, v, idx, out, lse, num_rows);
+  p.kv_len = kv_len;
+  p.num_reqs = 1;
+  if (legal == SA_OK_FALLBACK) {
+    // G * group > 32: the per-token path gives every row its own result
+    st = launch_attention(kernel, p, 0, stream);
+    return st == SA_OK ? ok(SA_ENTRY_PREFILL_UNION, SA_OK_FALLBACK) : st;
+  }
+  UnionLayout L;
+  if (!union_layout(num_rows, desc->topk, G, &L))
+    return fail(SA_ERR_SHAPE, "topk %d above %d", desc->topk, kMaxTopkPad);
+  if (!ws || ws_bytes < (size_t)L.total)
+    return fail(SA_ERR_WORKSPACE, "workspace of %zu bytes, %lld needed", ws_bytes,
+                (long long)L.total);
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(SA_ERR_SHAPE, "ws must be 256-byte aligned");
+  char* base = static_cast<char*>(ws);
+  sa::UnionBuildParams b =
+      build_params(idx, desc->idx_row_stride, num_rows, desc->topk, kv_len, G, L, ws);
+  b.union_idx = reinterpret_cast<int32_t*>(base + L.idx_off);
+  b.union_bits = reinterpret_cast<uint8_t*>(base + L.bits_off);
+  b.union_len = reinterpret_cast<int32_t*>(base + L.len_off);
+  b.union_stride = L.stride;
+  hipError_t e = sa::launch_union_build(b, stream);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  p.union_idx = b.union_idx;
+  p.union_bits = b.union_bits;
+  p.union_len = b.union_len;
+  p.union_stride = L.stride;
+  p.G = G;
+  p.num_groups = (int32_t)L.groups;
+  p.tokens_per_wave = 16 / p.group < G ? 16 / p.group : G;
+  p.waves_per_group = (G + p.tokens_per_wave - 1) / p.tokens_per_wave;
+  st = launch_attention(kernel, p, 2, stream);
+  return st == SA_OK ? ok(SA_ENTRY_PREFILL_UNION) : st;
 }
 
 sa_status page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src_pages,
                     int32_t src_page_tokens, int8_t* mask, hipStream_t stream) {
-  (void)idx; (void)num_idx; (void)num_src_pages; (void)src_page_tokens; (void)mask;
-  (void)stream;
-  return fail(SA_ERR_UNSUPPORTED, "page_mark not built yet");
+  g_err[0] = 0;
+  if (num_idx < 0 || num_src_pages < 0 || src_page_tokens <= 0)
+    return fail(SA_ERR_SHAPE, "num_idx %lld, num_src_pages %d, src_page_tokens %d",
+                (long long)num_idx, num_src_pages, src_page_tokens);
+  if (num_src_pages == 0) return ok(SA_ENTRY_PAGE_MARK);
+  if (!mask || (num_idx > 0 && !idx)) return fail(SA_ERR_NULL, "mask and idx are required");
+  if (reinterpret_cast<uintptr_t>(idx) & 3) return fail(SA_ERR_SHAPE, "idx must be 4-byte aligned");
+  if ((num_idx + 255) / 256 > INT32_MAX) return fail(SA_ERR_SHAPE, "too many indices");
+  const hipError_t e = sa::launch_page_mark(idx, num_idx, num_src_pages, src_page_tokens, mask,
+                                            stream);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok(SA_ENTRY_PAGE_MARK);
 }
 
 sa_status page_split(const sa_page_desc* desc, const uint8_t* src, uint8_t* dst,
                      const int8_t* mask, int32_t num_src_pages, hipStream_t stream) {
-  (void)desc; (void)src; (void)dst; (void)mask; (void)num_src_pages; (void)stream;
-  return fail(SA_ERR_UNSUPPORTED, "page_split not built yet");
+  g_err[0] = 0;
+  if (!desc) return fail(SA_ERR_NULL, "desc is NULL");
+  if (desc->src_page_tokens <= 0 || desc->dst_page_tokens <= 0 ||
+      desc->src_page_tokens % desc->dst_page_tokens || desc->row_bytes < 0 ||
+      desc->scale_bytes < 0 || num_src_pages < 0)
+    return fail(SA_ERR_SHAPE, "page geometry: src %d tokens must be a positive multiple of dst %d",
+                desc->src_page_tokens, desc->dst_page_tokens);
+  const int64_t src_bytes = (int64_t)desc->src_page_tokens * (desc->row_bytes + desc->scale_bytes);
+  const int64_t dst_bytes = (int64_t)desc->dst_page_tokens * (desc->row_bytes + desc->scale_bytes);
+  if (desc->src_page_stride < src_bytes || desc->dst_page_stride < dst_bytes)
+    return fail(SA_ERR_SHAPE, "page strides %lld / %lld below page sizes %lld / %lld",
+                (long long)desc->src_page_stride, (long long)desc->dst_page_stride,
+                (long long)src_bytes, (long long)dst_bytes);
+  const int64_t ratio = desc->src_page_tokens / desc->dst_page_tokens;
+  if ((int64_t)num_src_pages * ratio > INT32_MAX) return fail(SA_ERR_SHAPE, "too many pages");
+  if (num_src_pages == 0) return ok(SA_ENTRY_PAGE_SPLIT);
+  if (!src || !dst) return fail(SA_ERR_NULL, "src and dst are required");
+  sa::PageParams p{};
+  p.src = src;
+  p.dst = dst;
+  p.mask = mask;
+  p.src_page_stride = desc->src_page_stride;
+  p.dst_page_stride = desc->dst_page_stride;
+  p.num_src_pages = num_src_pages;
+  p.src_page_tokens = desc->src_page_tokens;
+  p.dst_page_tokens = desc->dst_page_tokens;
+  p.row_bytes = desc->row_bytes;
+  p.scale_bytes = desc->scale_bytes;
+  const hipError_t e = sa::launch_page_split(p, stream);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok(SA_ENTRY_PAGE_SPLIT);
 }
 
 }  // extern "C"

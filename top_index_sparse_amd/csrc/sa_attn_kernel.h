@@ -1,0 +1,305 @@
+// Index-gathered sparse attention forward: one kernel template for gfx950.
+//
+// What it computes (sglang PR 37275, "Motivation" and the mechanism note
+// under it; PR 32779, "Motivation" and "Modifications"): every query row
+// gathers its own selected K/V slots; the query heads that share a KV head
+// are padded into one 16-row matrix tile; the online softmax stays in
+// registers and no split partials reach HBM. In union mode several adjacent
+// rows share one deduplicated slot list, and a per-slot ownership bitmask
+// restores each row's own support (PR 32779, --dsa-triton-union).
+//
+// gfx950 design. One wavefront owns one 16-column tile of query rows (the
+// heads of one row for the per-token paths; up to 16 / group rows of a union
+// group for the union path) and streams that tile's slot list in tiles of 16
+// slots. The MFMA operand layouts are chosen so that every gathered byte goes
+// from global memory straight into the register where the matrix core wants
+// it, with no LDS and no barrier:
+//
+//   S^T[slot, col] = K_tile(16 x DQK) . Q^T(DQK x 16)       mfma 16x16x32 bf16
+//     lane (g = l/16, m = l%16) loads K row of slot m at d = 32s + 8g
+//     (s < DQK/32): four lanes read 64 contiguous bytes per instruction.
+//   P^T = exp2(S^T - max): the S^T accumulator (lane (g, n) holds slots
+//     4g..4g+3 of column n) is already the B operand of the next product.
+//   O^T[d, col] += V^T(16 x 16 slots) . P^T(16 slots x 16)   mfma 16x16x16 bf16
+//     lane (g, m) loads the V rows of slots 4g+i (i < 4) at bytes 256h + 16m
+//     (h < DV/128): sixteen lanes read 256 contiguous bytes of one row.
+//     In M-tile mt, row m of the A operand stands for
+//     d = 128(mt/8) + 8m + mt%8, element mt%8 of chunk mt/8 that the lane
+//     already holds, so V needs no transpose.
+//   All O^T accumulators of lane (g, n) belong to column n, whose running
+//   max and partial sum the lane holds after two cross-lane max steps per
+//   tile; the sum is accumulated from the unrounded fp32 probabilities.
+//
+// Four independent wavefronts form a workgroup; the block id is remapped so
+// that each XCD (own L2) works on a contiguous band of rows, which share
+// most of their slots. Invalid slots (outside [0, kv_len), past topk or
+// topk_len, or owned by none of the wave's rows) issue no memory traffic
+// and are masked to -inf before the softmax.
+#pragma once
+
+#include "sa_device.h"
+#include "sa_internal.h"
+
+namespace sa {
+
+enum : int { kPerToken = 0, kRagged = 1, kUnion = 2 };
+
+template <int DQK, int DV, bool V_IN_K, int MODE, int NBUF>
+struct AttnTile {
+  static constexpr int KSTEPS = DQK / 32;   // k-steps of the S^T product
+  static constexpr int VCH = DV / 128;      // 16-byte V chunks per slot per lane
+  static constexpr int MTILES = DV / 16;    // 16-wide d blocks of O^T
+  static_assert(DQK % 32 == 0 && DV % 128 == 0, "head dims");
+  static constexpr bool UNION = MODE == kUnion;
+
+  struct Idx {
+    int xk;          // slot m's index (K operand rows)
+    int xv[4];       // slots 4g..4g+3 (V operand rows, softmax columns)
+    uint32_t bk;     // ownership bits of slot m (union)
+    uint32_t bv;     // ownership bits of slots 4g..4g+3, one byte each (union)
+  };
+  struct Data {
+    u32x4_t kd[KSTEPS];
+    u32x4_t vd[4 * VCH];   // vd[VCH*i + h]: slot 4g+i, d = 128h + 8m .. +7
+    uint32_t vmask;        // bit i: slot 4g+i contributes to this lane's column
+  };
+};
+
+template <int DQK, int DV, bool V_IN_K, int MODE, int NBUF>
+__device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id) {
+  using TT = AttnTile<DQK, DV, V_IN_K, MODE, NBUF>;
+  constexpr int KSTEPS = TT::KSTEPS;
+  constexpr int VCH = TT::VCH;
+  constexpr int MTILES = TT::MTILES;
+  constexpr bool UNION = TT::UNION;
+  constexpr int TILE = 16;
+  using Idx = typename TT::Idx;
+  using Data = typename TT::Data;
+
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int group = p.group;
+
+  // ---- which rows this wave serves ------------------------------------
+  int kvh, t_col;            // KV head; query row of column n
+  bool col_live;             // column n is a real (row, head)
+  int head_col;              // query head of column n
+  uint32_t col_bit = 0;      // union: ownership bit of column n's row
+  uint32_t wave_bits = 0;    // union: bits of all rows this wave serves
+  const int32_t* irow;       // slot list
+  const uint8_t* brow = nullptr;
+  int jmax;
+  int64_t kv_base = 0;
+  int kv_len = p.kv_len;
+  if (UNION) {
+    const int per_head = p.num_groups * p.waves_per_group;
+    kvh = wave_id / per_head;
+    if (kvh >= p.num_kv_heads) return;
+    const int r = wave_id - kvh * per_head;
+    const int gi = r / p.waves_per_group;
+    const int ts = r - gi * p.waves_per_group;
+    const int j0 = ts * p.tokens_per_wave;                     // first member served
+    int members = p.G - j0;
+    if (members > p.tokens_per_wave) members = p.tokens_per_wave;
+    const int tail = p.num_rows - gi * p.G - j0;             // rows that exist
+    if (members > tail) members = tail;
+    if (members <= 0) return;
+    const int j = n / group;
+    col_live = j < members;
+    head_col = kvh * group + (n - j * group);
+    t_col = gi * p.G + j0 + (col_live ? j : 0);
+    col_bit = col_live ? (1u << (j0 + j)) : 0u;
+    wave_bits = ((1u << members) - 1u) << j0;
+    irow = p.union_idx + (int64_t)gi * p.union_stride;
+    brow = p.union_bits + (int64_t)gi * p.union_stride;
+    jmax = p.union_len[gi];
+  } else {
+    const int quads = (p.num_rows + 3) >> 2;
+    kvh = wave_id / (quads * 4);
+    const int t = wave_id - kvh * quads * 4;
+    if (t >= p.num_rows || kvh >= p.num_kv_heads) return;
+    col_live = n < group;
+    head_col = kvh * group + n;
+    t_col = t;
+    if (MODE == kRagged) {
+      int lo = 0, hi = p.num_reqs - 1;  // last request whose first row is <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      kv_base = p.cu_kv[lo];
+      kv_len = (int)(p.cu_kv[lo + 1] - kv_base);
+    }
+    irow = p.idx + (int64_t)t * p.idx_row_stride;
+    jmax = p.topk;
+    if (p.topk_len) {
+      const int tl = p.topk_len[t];
+      jmax = tl < 0 ? 0 : (tl < jmax ? tl : jmax);
+    }
+  }
+  if (kv_len <= 0) jmax = 0;
+  const int ntiles = (jmax + TILE - 1) / TILE;
+
+  const uint16_t* kbase = p.k + kv_base * p.k_row_stride + kvh * DQK + 8 * g;
+  const uint16_t* vbase = p.v + kv_base * p.v_row_stride + kvh * (V_IN_K ? DQK : DV) + 8 * n;
+
+  // ---- Q^T operand: lane (g, n) holds column n, d = 32s + 8g .. +7 -------
+  u32x4_t qop[KSTEPS];
+  {
+    const uint16_t* qp = p.q + (int64_t)t_col * p.q_row_stride + (int64_t)head_col * DQK + 8 * g;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      qop[s] = col_live ? ld16(qp + 32 * s) : (u32x4_t){0, 0, 0, 0};
+  }
+
+  auto load_idx = [&](Idx& ti, int j0) {
+    const int jk = j0 + n;
+    ti.xk = jk < jmax ? irow[jk] : -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int jv = j0 + 4 * g + i;
+      ti.xv[i] = jv < jmax ? irow[jv] : -1;
+    }
+    if (UNION) {
+      ti.bk = jk < jmax ? brow[jk] : 0u;
+      uint32_t b = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int jv = j0 + 4 * g + i;
+        b |= (jv < jmax ? (uint32_t)brow[jv] : 0u) << (8 * i);
+      }
+      ti.bv = b;
+    }
+  };
+
+  auto load_data = [&](Data& td, const Idx& ti) {
+    bool kok = (unsigned)ti.xk < (unsigned)kv_len;
+    if (UNION) kok = kok && (ti.bk & wave_bits);
+    const uint16_t* kp = kbase + (int64_t)(kok ? ti.xk : 0) * p.k_row_stride;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) td.kd[s] = (u32x4_t){0, 0, 0, 0};
+    if (kok) {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) td.kd[s] = ld16(kp + 32 * s);
+    }
+    uint32_t mask = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bool ok = (unsigned)ti.xv[i] < (unsigned)kv_len;
+      bool mine = ok;
+      if (UNION) {
+        const uint32_t b = (ti.bv >> (8 * i)) & 0xffu;
+        ok = ok && (b & wave_bits);
+        mine = ok && (b & col_bit);
+      }
+      mask |= (uint32_t)mine << i;
+      const uint16_t* vp = vbase + (int64_t)(ok ? ti.xv[i] : 0) * p.v_row_stride;
+#pragma unroll
+      for (int h = 0; h < VCH; ++h) td.vd[VCH * i + h] = (u32x4_t){0, 0, 0, 0};
+      if (ok) {
+#pragma unroll
+        for (int h = 0; h < VCH; ++h) td.vd[VCH * i + h] = ld16(vp + 128 * h);
+      }
+    }
+    td.vmask = mask;
+  };
+
+  float m_run = -INFINITY;  // running max of column n (log2 domain)
+  float l_run = 0.f;        // this lane's share of column n's running sum
+  f32x4_t acc[MTILES];
+#pragma unroll
+  for (int mt = 0; mt < MTILES; ++mt) acc[mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  const float c = p.scale_log2e;
+
+  auto compute = [&](const Data& td) {
+    f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) st = mfma_16x16x32(td.kd[s], qop[s], st);
+    float s2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s2[i] = ((td.vmask >> i) & 1u) ? st[i] * c : -INFINITY;
+    float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s2[i] - m_use);
+    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m_run = m_new;
+#pragma unroll
+    for (int mt = 0; mt < MTILES; ++mt) acc[mt] *= alpha;
+    const i16x4_t pop = __builtin_bit_cast(
+        i16x4_t, (u32x2_t){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
+#pragma unroll
+    for (int mt = 0; mt < MTILES; ++mt) {
+      const int h = mt >> 3, e = mt & 7;
+      const i16x4_t a = gather_col4(td.vd[h], td.vd[VCH + h], td.vd[2 * VCH + h],
+                                    td.vd[3 * VCH + h], e);
+      acc[mt] = mfma_16x16x16(a, pop, acc[mt]);
+    }
+  };
+
+  // Software pipeline over NBUF register buffers: before tile `cur` is
+  // consumed, the data loads of tile cur+NBUF-1 and the index loads of tile
+  // cur+NBUF are issued.
+  Idx ib[NBUF];
+  Data db[NBUF];
+#pragma unroll
+  for (int u = 0; u < NBUF; ++u)
+    if (u < ntiles) load_idx(ib[u], u * TILE);
+#pragma unroll
+  for (int u = 0; u + 1 < NBUF; ++u)
+    if (u < ntiles) load_data(db[u], ib[u]);
+  for (int tile = 0; tile < ntiles; tile += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      const int cur = tile + u;
+      if (cur >= ntiles) break;
+      const int nb = (u + NBUF - 1) % NBUF;
+      if (cur + NBUF - 1 < ntiles) {
+        load_data(db[nb], ib[nb]);
+        if (cur + NBUF < ntiles) load_idx(ib[u], (cur + NBUF) * TILE);
+      }
+      compute(db[u]);
+    }
+  }
+
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ---------------------
+  float l = l_run + __shfl_xor(l_run, 16);
+  l += __shfl_xor(l, 32);
+  if (col_live) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* orow = p.out + (int64_t)t_col * p.out_row_stride + (int64_t)head_col * DV;
+#pragma unroll
+    for (int h = 0; h < VCH; ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 128 * h + 32 * g + 8 * i;
+        const f32x4_t lo = {acc[8 * h + 0][i], acc[8 * h + 1][i], acc[8 * h + 2][i],
+                            acc[8 * h + 3][i]};
+        const f32x4_t hi = {acc[8 * h + 4][i], acc[8 * h + 5][i], acc[8 * h + 6][i],
+                            acc[8 * h + 7][i]};
+        st16(orow + d0, lo * inv);
+        st16(orow + d0 + 4, hi * inv);
+      }
+    }
+    if (g == 0)
+      p.lse[(int64_t)t_col * p.num_q_heads + head_col] =
+          l > 0.f ? (m_run + fast_log2(l)) * kLn2 : -INFINITY;
+  }
+}
+
+// Four wavefronts per workgroup, each an independent attn_wave.
+template <int DQK, int DV, bool V_IN_K, int MODE, int NBUF, int WAVES>
+__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
+                               amdgpu_waves_per_eu(WAVES, WAVES)))
+attn_kernel(AttnParams p) {
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  attn_wave<DQK, DV, V_IN_K, MODE, NBUF>(p, bid * 4 + (threadIdx.x >> 6));
+}
+
+}  // namespace sa

@@ -30,16 +30,15 @@ struct AttnParams {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   float scale_log2e;          // sm_scale * log2(e)
-};
-
-// Union attention over prebuilt union sets.
-struct UnionAttnParams {
-  AttnParams a;               // q, k, v, out, lse, strides, heads, scale
-  const int32_t* union_idx;   // [groups][union_stride]
-  const uint8_t* union_bits;  // [groups][union_stride]
-  const int32_t* union_len;   // [groups]
-  int64_t union_stride;       // G * topk
+  // union mode: prebuilt union sets of G adjacent rows
+  const int32_t* union_idx;   // [num_groups][union_stride]
+  const uint8_t* union_bits;  // [num_groups][union_stride]
+  const int32_t* union_len;   // [num_groups]
+  int64_t union_stride;
   int32_t G;
+  int32_t num_groups;
+  int32_t tokens_per_wave;    // rows of a group one wavefront serves
+  int32_t waves_per_group;
 };
 
 struct UnionBuildParams {
@@ -50,10 +49,11 @@ struct UnionBuildParams {
   int32_t kv_len;
   int32_t G;
   int32_t* sorted;            // workspace [num_rows][topk_pad]
-  int32_t topk_pad;
-  int32_t* union_idx;
-  uint8_t* union_bits;
-  int32_t* union_len;
+  int32_t topk_pad;           // power of two >= topk
+  int32_t* union_idx;         // [groups][union_stride], first G*topk used
+  uint8_t* union_bits;        // [groups][union_stride]
+  int32_t* union_len;         // [groups]
+  int64_t union_stride;
 };
 
 struct PageParams {
@@ -69,6 +69,12 @@ struct PageParams {
   int32_t scale_bytes;
 };
 
-hipError_t launch_gqa_d256(const AttnParams& p, bool ragged, hipStream_t stream);
+// mode: 0 per-token, 1 ragged chunk prefill, 2 union
+hipError_t launch_attn_gqa256(const AttnParams& p, int mode, hipStream_t stream);
+hipError_t launch_attn_mla576(const AttnParams& p, int mode, hipStream_t stream);
+hipError_t launch_union_build(const UnionBuildParams& p, hipStream_t stream);
+hipError_t launch_page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src_pages,
+                            int32_t src_page_tokens, int8_t* mask, hipStream_t stream);
+hipError_t launch_page_split(const PageParams& p, hipStream_t stream);
 
 }  // namespace sa

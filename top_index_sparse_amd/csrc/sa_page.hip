@@ -1,0 +1,90 @@
+// Decode-pool page mark and masked page split (sglang PR 32320,
+// "Modifications"): the pool keeps pages of src_page_tokens tokens; the
+// decode kernel reads pages of dst_page_tokens. The mark pass flags every
+// source page that a valid token index of the step falls in; the split pass
+// runs a fixed grid of one workgroup per destination page and returns at once
+// when its source page is unflagged, so only touched pages are copied and
+// the launch shape never depends on the data (no host read, graph safe).
+#include "sa_device.h"
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Clears the mask (a fill kernel rather than a memset node, so that a
+// captured graph replays it like any other kernel).
+__global__ void __launch_bounds__(kThreads) page_clear_kernel(int8_t* mask, int32_t n) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) mask[i] = 0;
+}
+
+// One thread per index: same-value stores of 1, no atomics needed.
+__global__ void __launch_bounds__(kThreads) page_mark_kernel(const int32_t* idx, int64_t num_idx,
+                                                             int64_t pool_tokens,
+                                                             int32_t src_page_tokens,
+                                                             int8_t* mask) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= num_idx) return;
+  const int32_t t = idx[i];
+  if (t >= 0 && (int64_t)t < pool_tokens) mask[t / src_page_tokens] = 1;
+}
+
+template <bool VEC16>
+__device__ __forceinline__ void copy_bytes(uint8_t* dst, const uint8_t* src, int64_t n) {
+  if (VEC16) {
+    const int64_t nv = n >> 4;
+    for (int64_t i = threadIdx.x; i < nv; i += kThreads)
+      reinterpret_cast<u32x4_t*>(dst)[i] = reinterpret_cast<const u32x4_t*>(src)[i];
+  } else {
+    for (int64_t i = threadIdx.x; i < n; i += kThreads) dst[i] = src[i];
+  }
+}
+
+// Workgroup (p, s) writes destination page p*ratio + s.
+template <bool VEC16>
+__global__ void __launch_bounds__(kThreads) page_split_kernel(PageParams p) {
+  const int ratio = p.src_page_tokens / p.dst_page_tokens;
+  const int page = blockIdx.x / ratio;
+  const int sub = blockIdx.x - page * ratio;
+  if (p.mask && p.mask[page] == 0) return;
+  const uint8_t* src = p.src + (int64_t)page * p.src_page_stride;
+  uint8_t* dst = p.dst + (int64_t)blockIdx.x * p.dst_page_stride;
+  const int64_t rows = (int64_t)p.dst_page_tokens * p.row_bytes;
+  const int64_t scales = (int64_t)p.dst_page_tokens * p.scale_bytes;
+  copy_bytes<VEC16>(dst, src + sub * rows, rows);
+  copy_bytes<VEC16>(dst + rows,
+                    src + (int64_t)p.src_page_tokens * p.row_bytes + sub * scales, scales);
+}
+
+}  // namespace
+
+hipError_t launch_page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src_pages,
+                            int32_t src_page_tokens, int8_t* mask, hipStream_t stream) {
+  hipLaunchKernelGGL(page_clear_kernel, dim3((unsigned)((num_src_pages + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, mask, num_src_pages);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || num_idx == 0) return e;
+  hipLaunchKernelGGL(page_mark_kernel, dim3((unsigned)((num_idx + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, stream, idx, num_idx,
+                     (int64_t)num_src_pages * src_page_tokens, src_page_tokens, mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_page_split(const PageParams& p, hipStream_t stream) {
+  const int ratio = p.src_page_tokens / p.dst_page_tokens;
+  const dim3 grid((unsigned)((int64_t)p.num_src_pages * ratio)), block(kThreads);
+  const int64_t rows = (int64_t)p.dst_page_tokens * p.row_bytes;
+  const int64_t scales = (int64_t)p.dst_page_tokens * p.scale_bytes;
+  const int64_t scale0 = (int64_t)p.src_page_tokens * p.row_bytes;
+  const bool vec = ((reinterpret_cast<uintptr_t>(p.src) | reinterpret_cast<uintptr_t>(p.dst)) & 15) == 0 &&
+                   ((p.src_page_stride | p.dst_page_stride | rows | scales | scale0) & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL(page_split_kernel<true>, grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL(page_split_kernel<false>, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace sa
