@@ -61,7 +61,7 @@ def gathered_bytes(case: gen.AttnCase) -> int:
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in ("sa_gqa.hip", "sa_device.h", "sa_internal.h"):
+    for name in ("sa_gqa.hip", "sa_attn_kernel.h", "sa_device.h", "sa_internal.h"):
         with open(os.path.join(ROOT, "top_index_sparse_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -123,6 +123,116 @@ def cpu_baseline(case: gen.AttnCase, stride: int, workers: int):
 
 # ------------------------------------------------------------------- GPU
 
+def _events_ms(torch, stream, fn, warmup, steps):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def _rate(nbytes, ms):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes": int(nbytes)}
+
+
+def measure_others(args, sa, torch, stream):
+    """Times every other workload once (HIP events on the launch stream)."""
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    res = {}
+    w, n = 3, 10
+    # group 12 over two KV heads, 131072-token context
+    c = gen.make_config("C2", args.seed)
+    q, k, v = bf16(c.q), bf16(c.k), bf16(c.v)
+    idx = torch.from_numpy(c.idx).cuda()
+    out = torch.empty((c.num_rows, c.num_q_heads, 256), dtype=torch.float32, device="cuda")
+    lse = torch.empty((c.num_rows, c.num_q_heads), dtype=torch.float32, device="cuda")
+    ms = _events_ms(torch, stream, lambda: sa.sparse_attn_prefill(
+        q, k, v, idx, sm_scale=c.scale, out=out, lse=lse, stream=stream), w, n)
+    res["group12_2kv_prefill"] = _rate(gathered_bytes(c), ms)
+    del q, k, v, idx, out, lse
+
+    # MLA per-token and union
+    c = gen.make_config("C3", args.seed)
+    q, k = bf16(c.q), bf16(c.k)
+    idx = torch.from_numpy(c.idx).cuda()
+    out = torch.empty((c.num_rows, c.num_q_heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((c.num_rows, c.num_q_heads), dtype=torch.float32, device="cuda")
+    per_token_bytes = gathered_bytes(c)
+    ms = _events_ms(torch, stream, lambda: sa.sparse_attn_prefill(
+        q, k, None, idx, sm_scale=c.scale, head_dim_v=512, out=out, lse=lse, stream=stream), w, n)
+    res["mla_per_token"] = _rate(per_token_bytes, ms)
+    for G in (2, 4):
+        ws = torch.empty(sa.sparse_attn_union_workspace_bytes(c.num_rows, c.topk, G),
+                         dtype=torch.uint8, device="cuda")
+        ui, ub, ul = sa.sparse_attn_union_build(idx, c.kv_len, G, ws=ws, stream=stream)
+        torch.cuda.synchronize()
+        rows = int(ul.sum().item())
+        ms_build = _events_ms(torch, stream, lambda: sa.sparse_attn_union_build(
+            idx, c.kv_len, G, union_idx=ui, union_bits=ub, union_len=ul, ws=ws, stream=stream),
+            w, n)
+        ms_all = _events_ms(torch, stream, lambda: sa.sparse_attn_prefill_union(
+            q, k, None, idx, G, sm_scale=c.scale, head_dim_v=512, ws=ws, out=out, lse=lse,
+            stream=stream), w, n)
+        r = _rate(rows * 1152, ms_all)
+        r.update({"union_rows": rows, "build_ms": round(ms_build, 4),
+                  "attention_ms": round(ms_all - ms_build, 4),
+                  "per_token_equivalent_GBps": round(per_token_bytes / (ms_all * 1e-3) / 1e9, 1),
+                  "speedup_vs_per_token": round(res["mla_per_token"]["ms"] / ms_all, 3)})
+        res[f"mla_union_G{G}"] = r
+        del ws, ui, ub, ul
+    del q, k, idx, out, lse
+
+    # ragged chunk prefill, 16 requests
+    c = gen.make_config("C4", args.seed)
+    q, k, v = bf16(c.q), bf16(c.k), bf16(c.v)
+    idx = torch.from_numpy(c.idx).cuda()
+    cu_q = torch.from_numpy(c.cu_seqlens_q).cuda()
+    cu_kv = torch.from_numpy(c.cu_seqlens_kv).cuda()
+    out = torch.empty((c.num_rows, c.num_q_heads, 256), dtype=torch.float32, device="cuda")
+    lse = torch.empty((c.num_rows, c.num_q_heads), dtype=torch.float32, device="cuda")
+    ms = _events_ms(torch, stream, lambda: sa.sparse_attn_chunk_prefill(
+        q, k, v, idx, cu_q, cu_kv, sm_scale=c.scale, out=out, lse=lse, stream=stream), w, n)
+    res["ragged_chunk_prefill"] = _rate(gathered_bytes(c), ms)
+    res["ragged_chunk_prefill"]["rows"] = c.num_rows
+    del q, k, v, idx, out, lse
+
+    # decode page mark + masked split vs full split
+    c = gen.make_config("C4decode", args.seed)
+    src = torch.from_numpy(c.src).cuda()
+    dst = torch.full((c.num_src_pages * c.ratio, c.dst_page_bytes), 0xA5, dtype=torch.uint8,
+                     device="cuda")
+    didx = torch.from_numpy(c.idx).cuda()
+    mask = torch.empty((c.num_src_pages,), dtype=torch.int8, device="cuda")
+    geom = dict(src_page_tokens=c.src_page_tokens, dst_page_tokens=c.dst_page_tokens,
+                row_bytes=c.row_bytes, scale_bytes=c.scale_bytes, stream=stream)
+    sa.page_mark(didx, c.num_src_pages, c.src_page_tokens, mask=mask, stream=stream)
+    torch.cuda.synchronize()
+    touched = int(mask.sum().item())
+    ms_mark = _events_ms(torch, stream, lambda: sa.page_mark(
+        didx, c.num_src_pages, c.src_page_tokens, mask=mask, stream=stream), w, n)
+    ms_split = _events_ms(torch, stream, lambda: sa.page_split(src, dst, mask, **geom), w, n)
+    ms_full = _events_ms(torch, stream, lambda: sa.page_split(src, dst, None, **geom), w, n)
+    page_bytes = c.src_page_bytes
+    res["decode_page_split"] = {
+        "touched_pages": touched, "mark_ms": round(ms_mark, 4),
+        "masked_split_ms": round(ms_split, 4), "full_split_ms": round(ms_full, 4),
+        "masked_GBps": round(2 * touched * page_bytes / (ms_split * 1e-3) / 1e9, 1),
+        "full_GBps": round(2 * c.num_src_pages * page_bytes / (ms_full * 1e-3) / 1e9, 1),
+        "full_frac_hbm_peak": round(2 * c.num_src_pages * page_bytes / (ms_full * 1e-3) / 1e9
+                                    / HBM_PEAK_GBS, 4)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,6 +245,9 @@ def main():
     ap.add_argument("--cpu-stride", type=int, default=2)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters)")
+    ap.add_argument("--others", choices=["on", "off"], default="on",
+                    help="also time the other workloads (group-12 prefill, MLA per-token "
+                         "and union, ragged chunk prefill, decode page mark/split)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -213,6 +326,8 @@ def main():
             print(json.dumps({"parity": parity}), file=sys.stderr)
             sys.exit(1)
 
+    others = measure_others(args, sa, torch, stream) if args.others == "on" else None
+
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     valid_slots = nbytes // 1024
     tflops = 2.0 * case.num_q_heads * valid_slots * (case.head_dim_qk + case.head_dim_v) \
@@ -247,6 +362,7 @@ def main():
         "kernel_ms": round(kernel_ms, 4),
         "tflops_useful": round(tflops, 2),
         "parity": parity,
+        "others": others,
     }
     print(json.dumps(result))
 
