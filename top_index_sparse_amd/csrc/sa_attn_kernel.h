@@ -30,9 +30,17 @@
 //   max and partial sum the lane holds after two cross-lane max steps per
 //   tile; the sum is accumulated from the unrounded fp32 probabilities.
 //
-// Four independent wavefronts form a workgroup; the block id is remapped so
-// that each XCD (own L2) works on a contiguous band of rows, which share
-// most of their slots. Invalid slots (outside [0, kv_len), past topk or
+// With WSPLIT = 2 a 16-column tile is shared by two wavefronts: each
+// computes half of the S^T k-steps (the two partial accumulators are summed
+// through a 2 KB LDS exchange, one barrier per slot tile, in the same order
+// in both waves so their softmax state stays bitwise identical) and half of
+// the O^T d-columns. That halves the registers per wavefront, so more
+// wavefronts (and more gathered bytes) are in flight per SIMD.
+//
+// With WSPLIT = 1, four independent wavefronts form a workgroup; with
+// WSPLIT = 2 a workgroup holds the wavefronts of one row (or one union
+// group). The block id is remapped so that each XCD (own L2) works on a
+// contiguous band of rows, which share most of their slots. Invalid slots (outside [0, kv_len), past topk or
 // topk_len, or owned by none of the wave's rows) issue no memory traffic
 // and are masked to -inf before the softmax.
 #pragma once
@@ -44,12 +52,12 @@ namespace sa {
 
 enum : int { kPerToken = 0, kRagged = 1, kUnion = 2 };
 
-template <int DQK, int DV, bool V_IN_K, int MODE, int NBUF>
+template <int DQK, int DV, bool V_IN_K, int MODE, int NBUF, int WSPLIT>
 struct AttnTile {
-  static constexpr int KSTEPS = DQK / 32;   // k-steps of the S^T product
-  static constexpr int VCH = DV / 128;      // 16-byte V chunks per slot per lane
-  static constexpr int MTILES = DV / 16;    // 16-wide d blocks of O^T
-  static_assert(DQK % 32 == 0 && DV % 128 == 0, "head dims");
+  static constexpr int KSTEPS = DQK / 32 / WSPLIT;   // this wave's k-steps of S^T
+  static constexpr int VCH = DV / 128 / WSPLIT;      // this wave's 16-byte V chunks per slot
+  static constexpr int MTILES = DV / 16 / WSPLIT;    // this wave's 16-wide d blocks of O^T
+  static_assert(DQK % (32 * WSPLIT) == 0 && DV % (128 * WSPLIT) == 0, "head dims");
   static constexpr bool UNION = MODE == kUnion;
 
   struct Idx {
@@ -65,9 +73,12 @@ struct AttnTile {
   };
 };
 
-template <int DQK, int DV, bool V_IN_K, int MODE, int NBUF>
-__device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id) {
-  using TT = AttnTile<DQK, DV, V_IN_K, MODE, NBUF>;
+// One 16-column tile of query rows (the virtual wave `wave_id`), or its half
+// `split` of WSPLIT. xch is the workgroup's exchange buffer [2][4][64].
+template <int DQK, int DV, bool V_IN_K, int MODE, int NBUF, int WSPLIT>
+__device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int split,
+                                          f32x4_t (*xch)[4][64]) {
+  using TT = AttnTile<DQK, DV, V_IN_K, MODE, NBUF, WSPLIT>;
   constexpr int KSTEPS = TT::KSTEPS;
   constexpr int VCH = TT::VCH;
   constexpr int MTILES = TT::MTILES;
@@ -104,13 +115,16 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id) {
     if (members > p.tokens_per_wave) members = p.tokens_per_wave;
     const int tail = p.num_rows - gi * p.G - j0;             // rows that exist
     if (members > tail) members = tail;
-    if (members <= 0) return;
+    if (members <= 0) {
+      if (WSPLIT == 1) return;
+      members = 0;     // keeps the workgroup's barriers matched; loads nothing
+    }
     const int j = n / group;
     col_live = j < members;
     head_col = kvh * group + (n - j * group);
     t_col = gi * p.G + j0 + (col_live ? j : 0);
     col_bit = col_live ? (1u << (j0 + j)) : 0u;
-    wave_bits = ((1u << members) - 1u) << j0;
+    wave_bits = ((1u << members) - 1u) << (members ? j0 : 0);
     irow = p.union_idx + (int64_t)gi * p.union_stride;
     brow = p.union_bits + (int64_t)gi * p.union_stride;
     jmax = p.union_len[gi];
@@ -141,13 +155,16 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id) {
   if (kv_len <= 0) jmax = 0;
   const int ntiles = (jmax + TILE - 1) / TILE;
 
-  const uint16_t* kbase = p.k + kv_base * p.k_row_stride + kvh * DQK + 8 * g;
-  const uint16_t* vbase = p.v + kv_base * p.v_row_stride + kvh * (V_IN_K ? DQK : DV) + 8 * n;
+  const int wv = threadIdx.x >> 6;
+  const uint16_t* kbase = p.k + kv_base * p.k_row_stride + kvh * DQK + 32 * KSTEPS * split + 8 * g;
+  const uint16_t* vbase =
+      p.v + kv_base * p.v_row_stride + kvh * (V_IN_K ? DQK : DV) + 128 * VCH * split + 8 * n;
 
   // ---- Q^T operand: lane (g, n) holds column n, d = 32s + 8g .. +7 -------
   u32x4_t qop[KSTEPS];
   {
-    const uint16_t* qp = p.q + (int64_t)t_col * p.q_row_stride + (int64_t)head_col * DQK + 8 * g;
+    const uint16_t* qp = p.q + (int64_t)t_col * p.q_row_stride + (int64_t)head_col * DQK +
+                         32 * KSTEPS * split + 8 * g;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
       qop[s] = col_live ? ld16(qp + 32 * s) : (u32x4_t){0, 0, 0, 0};
@@ -173,12 +190,14 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id) {
     }
   };
 
+  // Invalid slots skip their loads. Their K registers keep stale values
+  // (their scores are forced to -inf), and their V registers keep stale
+  // finite values from an earlier tile, or the zeros set before the loop,
+  // which are multiplied by p = 0.
   auto load_data = [&](Data& td, const Idx& ti) {
     bool kok = (unsigned)ti.xk < (unsigned)kv_len;
     if (UNION) kok = kok && (ti.bk & wave_bits);
     const uint16_t* kp = kbase + (int64_t)(kok ? ti.xk : 0) * p.k_row_stride;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) td.kd[s] = (u32x4_t){0, 0, 0, 0};
     if (kok) {
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) td.kd[s] = ld16(kp + 32 * s);
@@ -195,8 +214,6 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id) {
       }
       mask |= (uint32_t)mine << i;
       const uint16_t* vp = vbase + (int64_t)(ok ? ti.xv[i] : 0) * p.v_row_stride;
-#pragma unroll
-      for (int h = 0; h < VCH; ++h) td.vd[VCH * i + h] = (u32x4_t){0, 0, 0, 0};
       if (ok) {
 #pragma unroll
         for (int h = 0; h < VCH; ++h) td.vd[VCH * i + h] = ld16(vp + 128 * h);
@@ -212,10 +229,19 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id) {
   for (int mt = 0; mt < MTILES; ++mt) acc[mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   const float c = p.scale_log2e;
 
+  int par = 0;
   auto compute = [&](const Data& td) {
     f32x4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) st = mfma_16x16x32(td.kd[s], qop[s], st);
+    if (WSPLIT > 1) {
+      // partial S^T of the other half of d; both waves form half0 + half1
+      xch[par][wv][lane] = st;
+      __syncthreads();
+      const f32x4_t o = xch[par][wv ^ 1][lane];
+      st = split == 0 ? st + o : o + st;
+      par ^= 1;
+    }
     float s2[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) s2[i] = ((td.vmask >> i) & 1u) ? st[i] * c : -INFINITY;
@@ -229,9 +255,12 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s2[i] - m_use);
     l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m_run = m_new;
+    // Rescale only when some column's max moved (alpha == 1 elsewhere).
+    if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
 #pragma unroll
-    for (int mt = 0; mt < MTILES; ++mt) acc[mt] *= alpha;
+      for (int mt = 0; mt < MTILES; ++mt) acc[mt] *= alpha;
+    }
+    m_run = m_new;
     const i16x4_t pop = __builtin_bit_cast(
         i16x4_t, (u32x2_t){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
 #pragma unroll
@@ -243,28 +272,38 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id) {
     }
   };
 
-  // Software pipeline over NBUF register buffers: before tile `cur` is
-  // consumed, the data loads of tile cur+NBUF-1 and the index loads of tile
-  // cur+NBUF are issued.
-  Idx ib[NBUF];
+  // Software pipeline: NBUF data buffers, NBUF + 1 index buffers. At step
+  // `cur` the index loads of tile cur+NBUF are issued first, then the data
+  // loads of tile cur+NBUF-1 (whose indices arrived a step earlier), then
+  // tile cur is consumed. Loads retire in issue order, so issuing indices
+  // before data lets the data of NBUF-1 tiles stay in flight while the
+  // indices of the next one are awaited. The loop is unrolled NBUF*(NBUF+1)
+  // times so every buffer index is a compile-time constant.
+  constexpr int NI = NBUF + 1;
+  constexpr int UNROLL = NBUF * NI;
+  Idx ib[NI];
   Data db[NBUF];
+#pragma unroll
+  for (int u = 0; u < NBUF; ++u)
+#pragma unroll
+    for (int h = 0; h < 4 * VCH; ++h) db[u].vd[h] = (u32x4_t){0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < NBUF; ++u)
     if (u < ntiles) load_idx(ib[u], u * TILE);
 #pragma unroll
   for (int u = 0; u + 1 < NBUF; ++u)
     if (u < ntiles) load_data(db[u], ib[u]);
-  for (int tile = 0; tile < ntiles; tile += NBUF) {
+  for (int tile = 0; tile < ntiles; tile += UNROLL) {
 #pragma unroll
-    for (int u = 0; u < NBUF; ++u) {
+    for (int u = 0; u < UNROLL; ++u) {
       const int cur = tile + u;
       if (cur >= ntiles) break;
-      const int nb = (u + NBUF - 1) % NBUF;
-      if (cur + NBUF - 1 < ntiles) {
-        load_data(db[nb], ib[nb]);
-        if (cur + NBUF < ntiles) load_idx(ib[u], (cur + NBUF) * TILE);
-      }
-      compute(db[u]);
+      if (cur + NBUF < ntiles) load_idx(ib[(u + NBUF) % NI], (cur + NBUF) * TILE);
+      __builtin_amdgcn_sched_barrier(0);
+      if (cur + NBUF - 1 < ntiles)
+        load_data(db[(u + NBUF - 1) % NBUF], ib[(u + NBUF - 1) % NI]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(db[u % NBUF]);
     }
   }
 
@@ -278,7 +317,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id) {
     for (int h = 0; h < VCH; ++h) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int d0 = 128 * h + 32 * g + 8 * i;
+        const int d0 = 128 * (VCH * split + h) + 32 * g + 8 * i;
         const f32x4_t lo = {acc[8 * h + 0][i], acc[8 * h + 1][i], acc[8 * h + 2][i],
                             acc[8 * h + 3][i]};
         const f32x4_t hi = {acc[8 * h + 4][i], acc[8 * h + 5][i], acc[8 * h + 6][i],
@@ -287,19 +326,44 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id) {
         st16(orow + d0 + 4, hi * inv);
       }
     }
-    if (g == 0)
+    if (g == 0 && split == 0)
       p.lse[(int64_t)t_col * p.num_q_heads + head_col] =
           l > 0.f ? (m_run + fast_log2(l)) * kLn2 : -INFINITY;
   }
 }
 
-// Four wavefronts per workgroup, each an independent attn_wave.
-template <int DQK, int DV, bool V_IN_K, int MODE, int NBUF, int WAVES>
-__global__ void __attribute__((amdgpu_flat_work_group_size(256, 256),
+// WSPLIT = 1: four independent virtual waves per workgroup.
+// WSPLIT = 2: one row (per-token) or one union group per workgroup, whose
+// wavefronts are (column tile, split) pairs, split fastest.
+template <int DQK, int DV, bool V_IN_K, int MODE, int NBUF, int WSPLIT, int WAVES>
+__global__ void __attribute__((amdgpu_flat_work_group_size(64, 256),
                                amdgpu_waves_per_eu(WAVES, WAVES)))
 attn_kernel(AttnParams p) {
+  __shared__ f32x4_t xch[WSPLIT > 1 ? 2 : 1][4][64];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  attn_wave<DQK, DV, V_IN_K, MODE, NBUF>(p, bid * 4 + (threadIdx.x >> 6));
+  const int w = threadIdx.x >> 6;
+  if (WSPLIT == 1) {
+    attn_wave<DQK, DV, V_IN_K, MODE, NBUF, 1>(p, bid * 4 + w, 0, xch);
+  } else {
+    const int cols = MODE == kUnion ? p.waves_per_group : 1;
+    attn_wave<DQK, DV, V_IN_K, MODE, NBUF, WSPLIT>(p, bid * cols + w / WSPLIT, w % WSPLIT, xch);
+  }
+}
+
+// Workgroups and threads per workgroup for a launch.
+template <int WSPLIT>
+inline void attn_grid(const AttnParams& p, int mode, dim3* grid, dim3* block) {
+  const int64_t vwaves = mode == kUnion
+      ? (int64_t)p.num_groups * p.waves_per_group * p.num_kv_heads
+      : (int64_t)((p.num_rows + 3) / 4) * 4 * p.num_kv_heads;
+  if (WSPLIT == 1) {
+    *grid = dim3((unsigned)((vwaves + 3) / 4));
+    *block = dim3(256);
+  } else {
+    const int cols = mode == kUnion ? p.waves_per_group : 1;
+    *grid = dim3((unsigned)(vwaves / cols));
+    *block = dim3(64 * WSPLIT * cols);
+  }
 }
 
 }  // namespace sa

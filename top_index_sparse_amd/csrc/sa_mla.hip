@@ -7,31 +7,33 @@
 #define SA_MLA_NBUF 1
 #endif
 #ifndef SA_MLA_WAVES
-#define SA_MLA_WAVES 1
+#define SA_MLA_WAVES 2
+#endif
+#ifndef SA_MLA_WSPLIT
+#define SA_MLA_WSPLIT 2
 #endif
 
 namespace sa {
 
-constexpr int kMlaNbuf = SA_MLA_NBUF;
-constexpr int kMlaWaves = SA_MLA_WAVES;
+constexpr int kMlaNbuf = SA_MLA_NBUF;      // K/V tiles in flight per wavefront
+constexpr int kMlaWaves = SA_MLA_WAVES;    // wavefronts per SIMD the registers allow
+constexpr int kMlaWsplit = SA_MLA_WSPLIT;  // wavefronts sharing one 16-column tile
 
 hipError_t launch_attn_mla576(const AttnParams& p, int mode, hipStream_t stream) {
-  const int64_t waves = mode == kUnion
-      ? (int64_t)p.num_groups * p.waves_per_group * p.num_kv_heads
-      : (int64_t)((p.num_rows + 3) / 4) * 4 * p.num_kv_heads;
-  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  dim3 grid, block;
+  attn_grid<kMlaWsplit>(p, mode, &grid, &block);
   switch (mode) {
     case kPerToken:
-      hipLaunchKernelGGL((attn_kernel<576, 512, true, kPerToken, kMlaNbuf, kMlaWaves>), grid,
-                         block, 0, stream, p);
+      hipLaunchKernelGGL((attn_kernel<576, 512, true, kPerToken, kMlaNbuf, kMlaWsplit, kMlaWaves>),
+                         grid, block, 0, stream, p);
       break;
     case kRagged:
-      hipLaunchKernelGGL((attn_kernel<576, 512, true, kRagged, kMlaNbuf, kMlaWaves>), grid,
-                         block, 0, stream, p);
+      hipLaunchKernelGGL((attn_kernel<576, 512, true, kRagged, kMlaNbuf, kMlaWsplit, kMlaWaves>),
+                         grid, block, 0, stream, p);
       break;
     default:
-      hipLaunchKernelGGL((attn_kernel<576, 512, true, kUnion, kMlaNbuf, kMlaWaves>), grid,
-                         block, 0, stream, p);
+      hipLaunchKernelGGL((attn_kernel<576, 512, true, kUnion, kMlaNbuf, kMlaWsplit, kMlaWaves>),
+                         grid, block, 0, stream, p);
       break;
   }
   return hipGetLastError();
