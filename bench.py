@@ -150,6 +150,30 @@ def measure_others(args, sa, torch, stream):
 
     res = {}
     w, n = 3, 10
+    # union mode on the headline workload: two adjacent rows x 6 heads share
+    # one 16-column tile and one gather of their union
+    c = gen.make_config("C1", args.seed)
+    q, k, v = bf16(c.q), bf16(c.k), bf16(c.v)
+    idx = torch.from_numpy(c.idx).cuda()
+    out = torch.empty((c.num_rows, c.num_q_heads, 256), dtype=torch.float32, device="cuda")
+    lse = torch.empty((c.num_rows, c.num_q_heads), dtype=torch.float32, device="cuda")
+    per_token_bytes = gathered_bytes(c)
+    ws = torch.empty(sa.sparse_attn_union_workspace_bytes(c.num_rows, c.topk, 2),
+                     dtype=torch.uint8, device="cuda")
+    ui, ub, ul = sa.sparse_attn_union_build(idx, c.kv_len, 2, ws=ws, stream=stream)
+    torch.cuda.synchronize()
+    rows = int(ul.sum().item())
+    ms_build = _events_ms(torch, stream, lambda: sa.sparse_attn_union_build(
+        idx, c.kv_len, 2, union_idx=ui, union_bits=ub, union_len=ul, ws=ws, stream=stream), w, n)
+    ms_all = _events_ms(torch, stream, lambda: sa.sparse_attn_prefill_union(
+        q, k, v, idx, 2, sm_scale=c.scale, ws=ws, out=out, lse=lse, stream=stream), w, n)
+    r = _rate(rows * 1024, ms_all)
+    r.update({"union_rows": rows, "build_ms": round(ms_build, 4),
+              "attention_ms": round(ms_all - ms_build, 4),
+              "per_token_equivalent_GBps": round(per_token_bytes / (ms_all * 1e-3) / 1e9, 1)})
+    res["gqa_union_G2_same_workload"] = r
+    del q, k, v, idx, out, lse, ws, ui, ub, ul
+
     # group 12 over two KV heads, 131072-token context
     c = gen.make_config("C2", args.seed)
     q, k, v = bf16(c.q), bf16(c.k), bf16(c.v)

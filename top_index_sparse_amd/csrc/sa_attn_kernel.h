@@ -52,6 +52,7 @@ namespace sa {
 
 enum : int { kPerToken = 0, kRagged = 1, kUnion = 2 };
 
+
 template <int DQK, int DV, bool V_IN_K, int MODE, int NBUF, int WSPLIT>
 struct AttnTile {
   static constexpr int KSTEPS = DQK / 32 / WSPLIT;   // this wave's k-steps of S^T
@@ -61,10 +62,8 @@ struct AttnTile {
   static constexpr bool UNION = MODE == kUnion;
 
   struct Idx {
-    int xk;          // slot m's index (K operand rows)
-    int xv[4];       // slots 4g..4g+3 (V operand rows, softmax columns)
+    int xk;          // index of slot m; lanes 4g+i hold those of slots 4g+i
     uint32_t bk;     // ownership bits of slot m (union)
-    uint32_t bv;     // ownership bits of slots 4g..4g+3, one byte each (union)
   };
   struct Data {
     u32x4_t kd[KSTEPS];
@@ -156,9 +155,9 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
   const int ntiles = (jmax + TILE - 1) / TILE;
 
   const int wv = threadIdx.x >> 6;
-  const uint16_t* kbase = p.k + kv_base * p.k_row_stride + kvh * DQK + 32 * KSTEPS * split + 8 * g;
-  const uint16_t* vbase =
-      p.v + kv_base * p.v_row_stride + kvh * (V_IN_K ? DQK : DV) + 128 * VCH * split + 8 * n;
+  // Wave-uniform K/V bases; lane offsets are added per load.
+  const uint16_t* kw = p.k + kv_base * p.k_row_stride + kvh * DQK + 32 * KSTEPS * split;
+  const uint16_t* vw = p.v + kv_base * p.v_row_stride + kvh * (V_IN_K ? DQK : DV) + 128 * VCH * split;
 
   // ---- Q^T operand: lane (g, n) holds column n, d = 32s + 8g .. +7 -------
   u32x4_t qop[KSTEPS];
@@ -170,24 +169,13 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
       qop[s] = col_live ? ld16(qp + 32 * s) : (u32x4_t){0, 0, 0, 0};
   }
 
+  // One index (and ownership byte) load per lane per tile: lane (g, m)
+  // reads slot m; the V slots 4g..4g+3 come from lanes 4g..4g+3 by a
+  // cross-lane permute, which does not occupy the vector memory pipeline.
   auto load_idx = [&](Idx& ti, int j0) {
     const int jk = j0 + n;
     ti.xk = jk < jmax ? irow[jk] : -1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int jv = j0 + 4 * g + i;
-      ti.xv[i] = jv < jmax ? irow[jv] : -1;
-    }
-    if (UNION) {
-      ti.bk = jk < jmax ? brow[jk] : 0u;
-      uint32_t b = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int jv = j0 + 4 * g + i;
-        b |= (jv < jmax ? (uint32_t)brow[jv] : 0u) << (8 * i);
-      }
-      ti.bv = b;
-    }
+    if (UNION) ti.bk = jk < jmax ? (uint32_t)brow[jk] : 0u;
   };
 
   // Invalid slots skip their loads. Their K registers keep stale values
@@ -197,29 +185,40 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
   auto load_data = [&](Data& td, const Idx& ti) {
     bool kok = (unsigned)ti.xk < (unsigned)kv_len;
     if (UNION) kok = kok && (ti.bk & wave_bits);
-    const uint16_t* kp = kbase + (int64_t)(kok ? ti.xk : 0) * p.k_row_stride;
-    if (kok) {
+    int xv[4];
+    uint32_t bv[4];
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) td.kd[s] = ld16(kp + 32 * s);
+    for (int i = 0; i < 4; ++i) {
+      xv[i] = __builtin_amdgcn_ds_bpermute((4 * g + i) << 2, ti.xk);
+      if (UNION) bv[i] = (uint32_t)__builtin_amdgcn_ds_bpermute((4 * g + i) << 2, (int)ti.bk);
     }
+    bool vok[4];
     uint32_t mask = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      bool ok = (unsigned)ti.xv[i] < (unsigned)kv_len;
+      bool ok = (unsigned)xv[i] < (unsigned)kv_len;
       bool mine = ok;
       if (UNION) {
-        const uint32_t b = (ti.bv >> (8 * i)) & 0xffu;
-        ok = ok && (b & wave_bits);
-        mine = ok && (b & col_bit);
+        ok = ok && (bv[i] & wave_bits);
+        mine = ok && (bv[i] & col_bit);
       }
+      vok[i] = ok;
       mask |= (uint32_t)mine << i;
-      const uint16_t* vp = vbase + (int64_t)(ok ? ti.xv[i] : 0) * p.v_row_stride;
-      if (ok) {
+    }
+    td.vmask = mask;
+    if (kok) {
+      const uint16_t* kp = kw + (int64_t)ti.xk * p.k_row_stride + 8 * g;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) td.kd[s] = ld16(kp + 32 * s);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (vok[i]) {
+        const uint16_t* vp = vw + (int64_t)xv[i] * p.v_row_stride + 8 * n;
 #pragma unroll
         for (int h = 0; h < VCH; ++h) td.vd[VCH * i + h] = ld16(vp + 128 * h);
       }
     }
-    td.vmask = mask;
   };
 
   float m_run = -INFINITY;  // running max of column n (log2 domain)
@@ -341,7 +340,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(64, 256),
 attn_kernel(AttnParams p) {
   __shared__ f32x4_t xch[WSPLIT > 1 ? 2 : 1][4][64];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (WSPLIT == 1) {
     attn_wave<DQK, DV, V_IN_K, MODE, NBUF, 1>(p, bid * 4 + w, 0, xch);
   } else {
