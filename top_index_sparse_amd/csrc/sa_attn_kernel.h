@@ -38,8 +38,8 @@
 // wavefronts (and more gathered bytes) are in flight per SIMD.
 //
 // With WSPLIT = 1, four independent wavefronts form a workgroup; with
-// WSPLIT = 2 a workgroup holds the wavefronts of one row (or one union
-// group). The block id is remapped so that each XCD (own L2) works on a
+// WSPLIT = 2 a workgroup holds the two wavefronts of one column tile. The
+// block id is remapped so that each XCD (own L2) works on a
 // contiguous band of rows, which share most of their slots. Invalid slots (outside [0, kv_len), past topk or
 // topk_len, or owned by none of the wave's rows) issue no memory traffic
 // and are masked to -inf before the softmax.
@@ -60,13 +60,29 @@ struct AttnTile {
   static constexpr int MTILES = DV / 16 / WSPLIT;    // this wave's 16-wide d blocks of O^T
   static_assert(DQK % (32 * WSPLIT) == 0 && DV % (128 * WSPLIT) == 0, "head dims");
   static constexpr bool UNION = MODE == kUnion;
+  // V inside the latent K row: the wave's K slice is its V columns
+  // [split*MAIN, +MAIN) plus its rope columns [DV + split*ROPE, +ROPE), so V
+  // is part of the one gathered slice and both operands are read from LDS.
+  static constexpr int MAIN = DV / WSPLIT;
+  static constexpr int ROPE = (DQK - DV) / WSPLIT;
+  static constexpr bool VKLDS = V_IN_K && MAIN % 32 == 0 && ROPE % 32 == 0;
+  static constexpr int CPR = VKLDS ? (MAIN + ROPE) / 8 : 1;  // 16-byte chunks per slot row
+  // K staged through LDS when this wave's K slice is a whole number of
+  // 256-byte halves per slot (16 lanes x 16 B each).
+  static constexpr bool KLDS = !VKLDS && KSTEPS % 4 == 0;
+  static constexpr int KCH = KLDS ? KSTEPS / 4 : 0;   // 16-byte K chunks per slot per lane
+  static constexpr int KROW = 64 * KSTEPS + 16;       // LDS row pitch (bytes): 16 (mod 32) * odd
+  static constexpr int KLDS_BYTES = (KLDS || VKLDS) ? 16 * KROW : 16;
+  // wavefronts per workgroup: four independent column tiles, or the
+  // WSPLIT halves of one column tile
+  static constexpr int WG_WAVES = WSPLIT == 1 ? 4 : WSPLIT;
 
   struct Idx {
     int xk;          // index of slot m; lanes 4g+i hold those of slots 4g+i
     uint32_t bk;     // ownership bits of slot m (union)
   };
   struct Data {
-    u32x4_t kd[KSTEPS];
+    u32x4_t kd[KSTEPS];    // K operand rows (direct path) or raw 16-lane chunks (KLDS)
     u32x4_t vd[4 * VCH];   // vd[VCH*i + h]: slot 4g+i, d = 128h + 8m .. +7
     uint32_t vmask;        // bit i: slot 4g+i contributes to this lane's column
   };
@@ -76,12 +92,19 @@ struct AttnTile {
 // `split` of WSPLIT. xch is the workgroup's exchange buffer [2][4][64].
 template <int DQK, int DV, bool V_IN_K, int MODE, int NBUF, int WSPLIT>
 __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int split,
-                                          f32x4_t (*xch)[4][64]) {
+                                          f32x4_t (*xch)[64], uint8_t* klds) {
   using TT = AttnTile<DQK, DV, V_IN_K, MODE, NBUF, WSPLIT>;
   constexpr int KSTEPS = TT::KSTEPS;
   constexpr int VCH = TT::VCH;
   constexpr int MTILES = TT::MTILES;
   constexpr bool UNION = TT::UNION;
+  constexpr bool KLDS = TT::KLDS;
+  constexpr bool VKLDS = TT::VKLDS;
+  constexpr int KCH = TT::KCH;
+  constexpr int KROW = TT::KROW;
+  constexpr int MAIN = TT::MAIN;
+  constexpr int ROPE = TT::ROPE;
+  constexpr int CPR = TT::CPR;
   constexpr int TILE = 16;
   using Idx = typename TT::Idx;
   using Data = typename TT::Data;
@@ -114,16 +137,13 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
     if (members > p.tokens_per_wave) members = p.tokens_per_wave;
     const int tail = p.num_rows - gi * p.G - j0;             // rows that exist
     if (members > tail) members = tail;
-    if (members <= 0) {
-      if (WSPLIT == 1) return;
-      members = 0;     // keeps the workgroup's barriers matched; loads nothing
-    }
+    if (members <= 0) return;   // the whole workgroup (one column tile) leaves
     const int j = n / group;
     col_live = j < members;
     head_col = kvh * group + (n - j * group);
     t_col = gi * p.G + j0 + (col_live ? j : 0);
     col_bit = col_live ? (1u << (j0 + j)) : 0u;
-    wave_bits = ((1u << members) - 1u) << (members ? j0 : 0);
+    wave_bits = ((1u << members) - 1u) << j0;
     irow = p.union_idx + (int64_t)gi * p.union_stride;
     brow = p.union_bits + (int64_t)gi * p.union_stride;
     jmax = p.union_len[gi];
@@ -156,17 +176,20 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
 
   const int wv = threadIdx.x >> 6;
   // Wave-uniform K/V bases; lane offsets are added per load.
-  const uint16_t* kw = p.k + kv_base * p.k_row_stride + kvh * DQK + 32 * KSTEPS * split;
+  const uint16_t* kw = p.k + kv_base * p.k_row_stride + kvh * DQK + (VKLDS ? 0 : 32 * KSTEPS * split);
   const uint16_t* vw = p.v + kv_base * p.v_row_stride + kvh * (V_IN_K ? DQK : DV) + 128 * VCH * split;
 
   // ---- Q^T operand: lane (g, n) holds column n, d = 32s + 8g .. +7 -------
   u32x4_t qop[KSTEPS];
   {
-    const uint16_t* qp = p.q + (int64_t)t_col * p.q_row_stride + (int64_t)head_col * DQK +
-                         32 * KSTEPS * split + 8 * g;
+    const uint16_t* qp = p.q + (int64_t)t_col * p.q_row_stride + (int64_t)head_col * DQK + 8 * g;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-      qop[s] = col_live ? ld16(qp + 32 * s) : (u32x4_t){0, 0, 0, 0};
+    for (int s = 0; s < KSTEPS; ++s) {
+      // d of k-step s: the wave's slice in k-step order
+      const int d = VKLDS ? (s < MAIN / 32 ? split * MAIN + 32 * s : DV + split * ROPE + 32 * (s - MAIN / 32))
+                          : 32 * KSTEPS * split + 32 * s;
+      qop[s] = col_live ? ld16(qp + d) : (u32x4_t){0, 0, 0, 0};
+    }
   }
 
   // One index (and ownership byte) load per lane per tile: lane (g, m)
@@ -206,7 +229,27 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
       mask |= (uint32_t)mine << i;
     }
     td.vmask = mask;
-    if (kok) {
+    if (VKLDS) {
+      // Linear chunk order: load c covers chunks 64c .. 64c+63 of the tile's
+      // 16 slot rows (CPR chunks each), so consecutive lanes read
+      // consecutive 16-byte pieces of the same row.
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c) {
+        const int q = 64 * c + lane;
+        const int slot = q / CPR;
+        const int ch = q - slot * CPR;
+        // cross-lane reads first, with every lane active (a permute under a
+        // partial exec mask would read 0 from inactive source lanes)
+        const int x = __builtin_amdgcn_ds_bpermute(slot << 2, ti.xk);
+        const uint32_t b = UNION ? (uint32_t)__builtin_amdgcn_ds_bpermute(slot << 2, (int)ti.bk) : 0u;
+        bool ok = (unsigned)x < (unsigned)kv_len;
+        if (UNION) ok = ok && (b & wave_bits);
+        const int d = ch < MAIN / 8 ? split * MAIN + 8 * ch : DV + split * ROPE + 8 * (ch - MAIN / 8);
+        if (ok) td.kd[c] = ld16(kw + (int64_t)x * p.k_row_stride + d);
+      }
+      return;
+    }
+    if (!KLDS && kok) {
       const uint16_t* kp = kw + (int64_t)ti.xk * p.k_row_stride + 8 * g;
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) td.kd[s] = ld16(kp + 32 * s);
@@ -214,6 +257,12 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (vok[i]) {
+        if (KLDS) {
+          // K row of slot 4g+i, bytes 256h + 16m: sixteen lanes per row
+          const uint16_t* kp = kw + (int64_t)xv[i] * p.k_row_stride + 8 * n;
+#pragma unroll
+          for (int h = 0; h < KCH; ++h) td.kd[KCH * i + h] = ld16(kp + 128 * h);
+        }
         const uint16_t* vp = vw + (int64_t)xv[i] * p.v_row_stride + 8 * n;
 #pragma unroll
         for (int h = 0; h < VCH; ++h) td.vd[VCH * i + h] = ld16(vp + 128 * h);
@@ -229,15 +278,45 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
   const float c = p.scale_log2e;
 
   int par = 0;
+  uint8_t* lk = klds + wv * (16 * KROW);   // this wave's K tile in LDS
   auto compute = [&](const Data& td) {
     f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+    if (VKLDS) {
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) st = mfma_16x16x32(td.kd[s], qop[s], st);
+      for (int c = 0; c < KSTEPS; ++c) {
+        const int q = 64 * c + lane;
+        const int slot = q / CPR;
+        *reinterpret_cast<u32x4_t*>(lk + slot * KROW + 16 * (q - slot * CPR)) = td.kd[c];
+      }
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lk + n * KROW + 64 * s + 16 * g);
+        st = mfma_16x16x32(a, qop[s], st);
+      }
+    } else if (KLDS) {
+      // Transpose the gathered K rows into the MFMA A layout through LDS:
+      // write slot 4g+i, bytes 256h + 16m; read slot m, bytes 64s + 16g.
+      // The pitch KROW = 16 (mod 256) keeps both sides bank-conflict free.
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < KCH; ++h)
+          *reinterpret_cast<u32x4_t*>(lk + (4 * g + i) * KROW + 256 * h + 16 * n) = td.kd[KCH * i + h];
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lk + n * KROW + 64 * s + 16 * g);
+        st = mfma_16x16x32(a, qop[s], st);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) st = mfma_16x16x32(td.kd[s], qop[s], st);
+    }
     if (WSPLIT > 1) {
       // partial S^T of the other half of d; both waves form half0 + half1
-      xch[par][wv][lane] = st;
+      constexpr int WGW = TT::WG_WAVES;
+      xch[par * WGW + wv][lane] = st;
       __syncthreads();
-      const f32x4_t o = xch[par][wv ^ 1][lane];
+      const f32x4_t o = xch[par * WGW + (wv ^ 1)][lane];
       st = split == 0 ? st + o : o + st;
       par ^= 1;
     }
@@ -262,11 +341,17 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
     m_run = m_new;
     const i16x4_t pop = __builtin_bit_cast(
         i16x4_t, (u32x2_t){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
+    u32x4_t vv[4 * VCH];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < VCH; ++h)
+        vv[VCH * i + h] = VKLDS ? *reinterpret_cast<const u32x4_t*>(lk + (4 * g + i) * KROW + 256 * h + 16 * n)
+                                : td.vd[VCH * i + h];
 #pragma unroll
     for (int mt = 0; mt < MTILES; ++mt) {
       const int h = mt >> 3, e = mt & 7;
-      const i16x4_t a = gather_col4(td.vd[h], td.vd[VCH + h], td.vd[2 * VCH + h],
-                                    td.vd[3 * VCH + h], e);
+      const i16x4_t a = gather_col4(vv[h], vv[VCH + h], vv[2 * VCH + h], vv[3 * VCH + h], e);
       acc[mt] = mfma_16x16x16(a, pop, acc[mt]);
     }
   };
@@ -283,9 +368,14 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
   Idx ib[NI];
   Data db[NBUF];
 #pragma unroll
-  for (int u = 0; u < NBUF; ++u)
+  for (int u = 0; u < NBUF; ++u) {
 #pragma unroll
     for (int h = 0; h < 4 * VCH; ++h) db[u].vd[h] = (u32x4_t){0, 0, 0, 0};
+    if (VKLDS) {
+#pragma unroll
+      for (int c = 0; c < KSTEPS; ++c) db[u].kd[c] = (u32x4_t){0, 0, 0, 0};
+    }
+  }
 #pragma unroll
   for (int u = 0; u < NBUF; ++u)
     if (u < ntiles) load_idx(ib[u], u * TILE);
@@ -331,22 +421,22 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
   }
 }
 
-// WSPLIT = 1: four independent virtual waves per workgroup.
-// WSPLIT = 2: one row (per-token) or one union group per workgroup, whose
-// wavefronts are (column tile, split) pairs, split fastest.
+// WSPLIT = 1: four independent column tiles ("virtual waves") per
+// workgroup. WSPLIT = 2: one column tile per workgroup, its two halves on
+// two wavefronts that exchange partial scores through LDS.
 template <int DQK, int DV, bool V_IN_K, int MODE, int NBUF, int WSPLIT, int WAVES>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64, 256),
                                amdgpu_waves_per_eu(WAVES, WAVES)))
 attn_kernel(AttnParams p) {
-  __shared__ f32x4_t xch[WSPLIT > 1 ? 2 : 1][4][64];
+  using TT = AttnTile<DQK, DV, V_IN_K, MODE, NBUF, WSPLIT>;
+  __shared__ f32x4_t xch[(WSPLIT > 1 ? 2 : 1) * TT::WG_WAVES][64];
+  __shared__ __attribute__((aligned(16))) uint8_t klds[TT::WG_WAVES * TT::KLDS_BYTES];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (WSPLIT == 1) {
-    attn_wave<DQK, DV, V_IN_K, MODE, NBUF, 1>(p, bid * 4 + w, 0, xch);
-  } else {
-    const int cols = MODE == kUnion ? p.waves_per_group : 1;
-    attn_wave<DQK, DV, V_IN_K, MODE, NBUF, WSPLIT>(p, bid * cols + w / WSPLIT, w % WSPLIT, xch);
-  }
+  if (WSPLIT == 1)
+    attn_wave<DQK, DV, V_IN_K, MODE, NBUF, 1>(p, bid * 4 + w, 0, xch, klds);
+  else
+    attn_wave<DQK, DV, V_IN_K, MODE, NBUF, WSPLIT>(p, bid, w, xch, klds);
 }
 
 // Workgroups and threads per workgroup for a launch.
@@ -359,9 +449,8 @@ inline void attn_grid(const AttnParams& p, int mode, dim3* grid, dim3* block) {
     *grid = dim3((unsigned)((vwaves + 3) / 4));
     *block = dim3(256);
   } else {
-    const int cols = mode == kUnion ? p.waves_per_group : 1;
-    *grid = dim3((unsigned)(vwaves / cols));
-    *block = dim3(64 * WSPLIT * cols);
+    *grid = dim3((unsigned)vwaves);
+    *block = dim3(64 * WSPLIT);
   }
 }
 
