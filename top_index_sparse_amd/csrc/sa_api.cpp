@@ -150,7 +150,7 @@ struct UnionLayout {
 
 bool union_layout(int32_t num_rows, int32_t topk, int32_t G, UnionLayout* L) {
   if (num_rows < 0 || topk <= 0 || G < 1 || G > 8) return false;
-  L->topk_pad = pow2_at_least(topk < 2 ? 2 : topk);
+  L->topk_pad = pow2_at_least(topk < 256 ? 256 : topk);
   if (L->topk_pad > kMaxTopkPad) return false;
   L->groups = (num_rows + G - 1) / G;
   L->stride = align_up((int64_t)G * topk, 16);

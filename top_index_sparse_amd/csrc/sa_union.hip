@@ -10,47 +10,87 @@
 // distinct valid indices ascending, then row 1's new ones ascending, ...,
 // then -1; union_bits[g][r] has bit j set iff row j of the group selected
 // union_idx[g][r]; union_len[g] counts the listed indices.
+//
+// gfx950 design.
+//   Sort: one wavefront per row holds the row's N = 64R keys in registers
+//   (lane l owns keys lR .. lR+R-1). A bitonic network runs its
+//   compare-exchanges between registers of one lane when the partner
+//   distance is below R and between lanes by shuffles otherwise, so the
+//   sort needs no barrier. The coalesced load reaches that blocked layout
+//   through a wave-private LDS buffer.
+//   Merge: one workgroup per group stages the members' sorted lists in LDS
+//   (global memory when they exceed 64 KB); each thread takes 8 consecutive
+//   keys of one list, binary-searches the first in every other list and
+//   walks forward for the rest. A block-wide scan of the emit flags gives
+//   every emitted key its output slot.
 #include "sa_device.h"
 #include "sa_internal.h"
 
 namespace sa {
 namespace {
 
-constexpr int kSortThreads = 256;
 constexpr int kMergeThreads = 256;
-constexpr int kItems = 8;           // consecutive list entries per merge thread
+constexpr int kItems = 8;             // consecutive list entries per merge thread
 constexpr int32_t kEmpty = 0x7fffffff;
+constexpr int kMergeLdsMax = 65536;   // bytes of sorted lists staged in LDS
 
-// Sort kernel: one workgroup per row; bitonic sort of topk_pad keys in LDS.
-// Invalid indices (outside [0, kv_len)) become kEmpty and sort last.
-__global__ void __launch_bounds__(kSortThreads) union_sort_kernel(UnionBuildParams p) {
-  extern __shared__ int32_t keys[];
+template <int R>
+__global__ void __launch_bounds__(64) union_sort_kernel(UnionBuildParams p) {
+  constexpr int N = 64 * R;
+  static_assert(R >= 4 && (R & (R - 1)) == 0, "keys per lane");
+  __shared__ __attribute__((aligned(16))) int32_t sh[N];
+  const int lane = threadIdx.x;
   const int t = blockIdx.x;
-  const int N = p.topk_pad;
   const int32_t* row = p.idx + (int64_t)t * p.idx_row_stride;
-  for (int i = threadIdx.x; i < N; i += kSortThreads) {
-    const int32_t x = i < p.topk ? row[i] : -1;
-    keys[i] = (unsigned)x < (unsigned)p.kv_len ? x : kEmpty;
+  // Invalid indices (outside [0, kv_len)) become kEmpty and sort last.
+#pragma unroll 8
+  for (int r = 0; r < R; ++r) {
+    const int e = r * 64 + lane;
+    const int32_t x = e < p.topk ? row[e] : -1;
+    sh[e] = (unsigned)x < (unsigned)p.kv_len ? x : kEmpty;
   }
-  __syncthreads();
+  int32_t key[R];
+#pragma unroll
+  for (int r = 0; r < R; r += 4) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(sh + lane * R + r);
+    key[r] = (int32_t)v[0];
+    key[r + 1] = (int32_t)v[1];
+    key[r + 2] = (int32_t)v[2];
+    key[r + 3] = (int32_t)v[3];
+  }
   for (int k = 2; k <= N; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < (N >> 1); i += kSortThreads) {
-        // i-th compare-exchange pair of this stage: lo has bit j clear
-        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-        const int hi = lo | j;
-        const bool ascending = (lo & k) == 0;
-        const int32_t a = keys[lo], b = keys[hi];
-        if ((a > b) == ascending) {
-          keys[lo] = b;
-          keys[hi] = a;
+    // partner element e ^ j lives in lane ^ (j / R), same register
+    for (int j = k >> 1; j >= R; j >>= 1) {
+      const int d = j / R;
+      const bool lower = (lane & d) == 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int32_t o = __shfl_xor(key[r], d);
+        const bool asc = ((lane * R + r) & k) == 0;
+        key[r] = (asc == lower) ? min(key[r], o) : max(key[r], o);
+      }
+    }
+    // partner in the same lane: registers r and r + j
+#pragma unroll
+    for (int j = R / 2; j >= 1; j >>= 1) {
+      if (j < k) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (r & j) continue;
+          const bool asc = ((lane * R + r) & k) == 0;
+          const int32_t a = key[r], b = key[r + j];
+          const int32_t lo = min(a, b), hi = max(a, b);
+          key[r] = asc ? lo : hi;
+          key[r + j] = asc ? hi : lo;
         }
       }
-      __syncthreads();
     }
   }
-  int32_t* out = p.sorted + (int64_t)t * N;
-  for (int i = threadIdx.x; i < N; i += kSortThreads) out[i] = keys[i];
+  int32_t* out = p.sorted + (int64_t)t * N + lane * R;
+#pragma unroll
+  for (int r = 0; r < R; r += 4)
+    *reinterpret_cast<u32x4_t*>(out + r) =
+        (u32x4_t){(uint32_t)key[r], (uint32_t)key[r + 1], (uint32_t)key[r + 2], (uint32_t)key[r + 3]};
 }
 
 // First position in the sorted list s[0..n) whose key is >= x.
@@ -68,10 +108,11 @@ __device__ __forceinline__ int lower_bound(const int32_t* s, int n, int32_t x) {
   return lo;
 }
 
-// Merge kernel: one workgroup per group. The group's lists are walked in
-// the output order (row-major, ascending within a row); a block-wide scan
-// of the emit flags gives every emitted index its output slot.
+// One workgroup per group. The group's lists are walked in the output order
+// (row-major, ascending within a row).
+template <bool LDS>
 __global__ void __launch_bounds__(kMergeThreads) union_merge_kernel(UnionBuildParams p) {
+  extern __shared__ __attribute__((aligned(16))) int32_t staged[];
   __shared__ int32_t warp_sums[kMergeThreads / 64];
   __shared__ int32_t carry_s;
   const int gi = blockIdx.x;
@@ -79,7 +120,14 @@ __global__ void __launch_bounds__(kMergeThreads) union_merge_kernel(UnionBuildPa
   const int first = gi * p.G;
   int members = p.num_rows - first;
   if (members > p.G) members = p.G;
-  const int32_t* lists = p.sorted + (int64_t)first * N;
+  const int32_t* src = p.sorted + (int64_t)first * N;
+  const int total_items = members * N;
+  const int32_t* lists = src;
+  if (LDS) {
+    for (int i = threadIdx.x * 4; i < total_items; i += kMergeThreads * 4)
+      *reinterpret_cast<u32x4_t*>(staged + i) = *reinterpret_cast<const u32x4_t*>(src + i);
+    lists = staged;
+  }
   const int64_t width = (int64_t)p.G * p.topk;
   int32_t* uidx = p.union_idx + (int64_t)gi * p.union_stride;
   uint8_t* ubits = p.union_bits + (int64_t)gi * p.union_stride;
@@ -87,42 +135,50 @@ __global__ void __launch_bounds__(kMergeThreads) union_merge_kernel(UnionBuildPa
   if (threadIdx.x == 0) carry_s = 0;
   __syncthreads();
 
-  const int total_items = members * N;
   const int chunk = kMergeThreads * kItems;
   for (int base = 0; base < total_items; base += chunk) {
     int32_t xs[kItems];
     uint32_t bits[kItems];
-    int count = 0;
-    const int start = base + threadIdx.x * kItems;
+    const int start = base + threadIdx.x * kItems;   // all items in one list (N % 8 == 0)
+    const int j = start / N;
+    const int k0 = start - j * N;
+    const int32_t* s = lists + (int64_t)j * N;
+    bool live[kItems];
 #pragma unroll
     for (int e = 0; e < kItems; ++e) {
-      const int pos = start + e;
       xs[e] = kEmpty;
       bits[e] = 0;
-      if (pos < total_items) {
-        const int j = pos / N, k = pos - j * N;
-        const int32_t* s = lists + (int64_t)j * N;
-        const int32_t x = s[k];
-        const bool live = x != kEmpty && (k == 0 || s[k - 1] != x);
-        if (live) {
-          uint32_t b = 1u << j;
-          bool earlier = false;
-          for (int jj = 0; jj < members; ++jj) {
-            if (jj == j) continue;
-            const int32_t* o = lists + (int64_t)jj * N;
-            const int at = lower_bound(o, N, x);
-            if (at < N && o[at] == x) {
-              b |= 1u << jj;
-              earlier |= jj < j;
-            }
-          }
-          if (!earlier) {
-            xs[e] = x;
-            bits[e] = b;
-            ++count;
+      live[e] = false;
+      if (start + e < total_items) {
+        const int32_t x = s[k0 + e];
+        live[e] = x != kEmpty && (k0 + e == 0 || s[k0 + e - 1] != x);
+        xs[e] = x;
+        bits[e] = 1u << j;
+      }
+    }
+    bool earlier[kItems];
+#pragma unroll
+    for (int e = 0; e < kItems; ++e) earlier[e] = false;
+    if (start < total_items) {
+      for (int jj = 0; jj < members; ++jj) {
+        if (jj == j) continue;
+        const int32_t* o = lists + (int64_t)jj * N;
+        int at = lower_bound(o, N, xs[0]);
+#pragma unroll
+        for (int e = 0; e < kItems; ++e) {
+          while (at < N && o[at] < xs[e]) ++at;     // keys ascend within the thread
+          if (live[e] && at < N && o[at] == xs[e]) {
+            bits[e] |= 1u << jj;
+            earlier[e] |= jj < j;
           }
         }
       }
+    }
+    int count = 0;
+#pragma unroll
+    for (int e = 0; e < kItems; ++e) {
+      live[e] = live[e] && !earlier[e];
+      count += live[e];
     }
     // block-wide exclusive scan of the per-thread counts
     int incl = count;
@@ -142,7 +198,7 @@ __global__ void __launch_bounds__(kMergeThreads) union_merge_kernel(UnionBuildPa
     int out = carry_s + wave_base + incl - count;
 #pragma unroll
     for (int e = 0; e < kItems; ++e) {
-      if (bits[e]) {
+      if (live[e]) {
         uidx[out] = xs[e];
         ubits[out] = (uint8_t)bits[e];
         ++out;
@@ -160,16 +216,31 @@ __global__ void __launch_bounds__(kMergeThreads) union_merge_kernel(UnionBuildPa
   if (threadIdx.x == 0) p.union_len[gi] = len;
 }
 
+template <int R>
+void launch_sort(const UnionBuildParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(union_sort_kernel<R>, dim3((unsigned)p.num_rows), dim3(64), 0, stream, p);
+}
+
 }  // namespace
 
 hipError_t launch_union_build(const UnionBuildParams& p, hipStream_t stream) {
-  const size_t lds = (size_t)p.topk_pad * sizeof(int32_t);
-  hipLaunchKernelGGL(union_sort_kernel, dim3((unsigned)p.num_rows), dim3(kSortThreads), lds,
-                     stream, p);
+  switch (p.topk_pad) {
+    case 256: launch_sort<4>(p, stream); break;
+    case 512: launch_sort<8>(p, stream); break;
+    case 1024: launch_sort<16>(p, stream); break;
+    case 2048: launch_sort<32>(p, stream); break;
+    case 4096: launch_sort<64>(p, stream); break;
+    case 8192: launch_sort<128>(p, stream); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned groups = (unsigned)((p.num_rows + p.G - 1) / p.G);
-  hipLaunchKernelGGL(union_merge_kernel, dim3(groups), dim3(kMergeThreads), 0, stream, p);
+  const size_t lists = (size_t)p.G * p.topk_pad * sizeof(int32_t);
+  if (lists <= (size_t)kMergeLdsMax)
+    hipLaunchKernelGGL(union_merge_kernel<true>, dim3(groups), dim3(kMergeThreads), lists, stream, p);
+  else
+    hipLaunchKernelGGL(union_merge_kernel<false>, dim3(groups), dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 
