@@ -69,13 +69,22 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).
-// Remap so that XCD x runs a contiguous band of logical block ids, keeping
-// neighbouring rows (which share most of their indices) in one L2.
+// Remap so that each XCD runs chunks of kXcdChunk consecutive logical blocks
+// (neighbouring rows share most of their slots, so they should share an
+// L2), with the chunks dealt round-robin to the XCDs so every XCD gets work
+// from the whole range (rows with short visible prefixes carry less work).
+// The last, partial round of chunks is split into contiguous bands.
+constexpr int kXcdChunk = 64;
+
 __device__ __forceinline__ int xcd_remap(int b, int nblk) {
   constexpr int X = 8;
-  const int q = nblk / X, r = nblk % X;
   const int xcd = b % X, local = b / X;
-  return xcd * q + (xcd < r ? xcd : r) + local;
+  const int rounds = nblk / (X * kXcdChunk);
+  if (local < rounds * kXcdChunk)
+    return (local / kXcdChunk) * (X * kXcdChunk) + xcd * kXcdChunk + local % kXcdChunk;
+  const int tail = nblk - rounds * X * kXcdChunk;
+  const int q = tail / X, r = tail % X;
+  return rounds * X * kXcdChunk + xcd * q + (xcd < r ? xcd : r) + (local - rounds * kXcdChunk);
 }
 
 }  // namespace sa

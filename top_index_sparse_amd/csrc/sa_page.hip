@@ -31,12 +31,25 @@ __global__ void __launch_bounds__(kThreads) page_mark_kernel(const int32_t* idx,
   if (t >= 0 && (int64_t)t < pool_tokens) mask[t / src_page_tokens] = 1;
 }
 
+// Copies n bytes; eight 16-byte loads per thread are issued before their
+// stores so that a page costs about two memory round trips, not eleven.
 template <bool VEC16>
-__device__ __forceinline__ void copy_bytes(uint8_t* dst, const uint8_t* src, int64_t n) {
+__device__ __forceinline__ void copy_bytes(uint8_t* __restrict__ dst, const uint8_t* __restrict__ src,
+                                           int64_t n) {
   if (VEC16) {
+    constexpr int U = 8;
     const int64_t nv = n >> 4;
-    for (int64_t i = threadIdx.x; i < nv; i += kThreads)
-      reinterpret_cast<u32x4_t*>(dst)[i] = reinterpret_cast<const u32x4_t*>(src)[i];
+    const u32x4_t* s = reinterpret_cast<const u32x4_t*>(src);
+    u32x4_t* d = reinterpret_cast<u32x4_t*>(dst);
+    for (int64_t i = threadIdx.x; i < nv; i += U * kThreads) {
+      u32x4_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (i + u * kThreads < nv) v[u] = s[i + u * kThreads];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (i + u * kThreads < nv) d[i + u * kThreads] = v[u];
+    }
   } else {
     for (int64_t i = threadIdx.x; i < n; i += kThreads) dst[i] = src[i];
   }
