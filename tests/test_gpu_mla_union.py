@@ -143,10 +143,17 @@ def test_union_mla_c3_sampled(G):
     sel = torch.from_numpy(rows).cuda()
     e, el = check_close(out[sel], lse[sel], ro, rl, f"union G={G}")
     assert torch.isfinite(out).all()
-    # the per-token path on the same rows (duplicate-free rows: same result)
+    # The per-token path on every row: duplicate-free rows give the same
+    # result up to summation order. LSE is the sensitive check (one slot
+    # more or less moves it by ~1/topk); O differs by the bf16 rounding of
+    # P taken against different running maxima.
     po, pl = _prefill(case, dev)
-    assert (out - po).abs().max().item() < 2e-3
-    assert (lse - pl).abs().max().item() < 2e-5
+    dl = (lse - pl).abs()
+    do = (out.float() - po.float()).abs()
+    say(f"  union vs per-token: max |dLSE| {dl.max().item():.2e} at row "
+        f"{int(dl.amax(1).argmax())}, max |dO| {do.max().item():.2e}")
+    assert dl.max().item() < 2e-5
+    assert (do <= 2e-2 + 1e-2 * po.float().abs()).all()
     say(f"  C3 G={G}: max abs err O {e:.2e} LSE {el:.2e}")
 
 

@@ -223,3 +223,30 @@ def test_chunk_prefill_c4_sampled():
     e, el = check_close(out[sel], lse[sel], ro, rl, "C4")
     assert torch.isfinite(out).all()
     say(f"  C4: max abs err O {e:.2e}  LSE {el:.2e} over {len(rows)} rows")
+
+
+def test_paired_rows_with_disjoint_positions():
+    say("[prefill] row pairs: same sets at shifted positions, cross-position duplicates")
+    case = _small(16, 24, 1500, 1400, 6, 1, 200)
+    idx = case.idx.copy()
+    for t in range(1, 24, 2):
+        idx[t] = np.roll(idx[t - 1], 7)            # same set, no position matches
+    idx[3, :50] = idx[2, 100:150]                  # matches at other positions only
+    idx[5, ::2] = idx[4, ::2]                      # half the positions match
+    idx[5, 1::2] = -1
+    idx[7, :] = idx[6, :]                          # identical rows
+    idx[9, 10:30] = idx[9, 9]                      # duplicates inside the second row
+    idx[11] = -1                                   # empty second row
+    case.idx = idx
+    dev = attn_to_dev(case)
+    out, lse = _run_prefill(case, dev)
+    ro, rl = _oracle(case)
+    check_close(out, lse, ro, rl, "paired positions")
+    cu_q = i32_dev(np.array([0, 5, 5, 24]))        # pairs that straddle requests
+    cu_kv = i64_dev(np.array([0, 1500, 1500, 3000]))
+    k2 = torch.cat([dev["k"], dev["k"]])
+    v2 = torch.cat([dev["v"], dev["v"]])
+    o2, l2 = sa.sparse_attn_chunk_prefill(dev["q"], k2, v2, dev["idx"], cu_q, cu_kv,
+                                          sm_scale=case.scale)
+    torch.cuda.synchronize()
+    check_close(o2, l2, ro, rl, "paired ragged")

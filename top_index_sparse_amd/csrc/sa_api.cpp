@@ -212,7 +212,9 @@ sa_status sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const voi
   p.topk_len = topk_len;
   p.kv_len = kv_len;
   p.num_reqs = 1;
-  st = launch_attention(kernel, p, 0, stream);
+  // Two rows per wavefront share the gathers of their common slots when
+  // both rows' heads fit one 16-column tile.
+  st = launch_attention(kernel, p, 2 * p.group <= 16 ? 3 : 0, stream);
   return st == SA_OK ? ok(SA_ENTRY_PREFILL) : st;
 }
 
@@ -238,7 +240,7 @@ sa_status sparse_attn_chunk_prefill(const sa_attn_desc* desc, const void* q, con
   p.cu_q = cu_seqlens_q;
   p.cu_kv = cu_seqlens_kv;
   p.num_reqs = num_reqs;
-  st = launch_attention(kernel, p, 1, stream);
+  st = launch_attention(kernel, p, 2 * p.group <= 16 ? 4 : 1, stream);
   return st == SA_OK ? ok(SA_ENTRY_CHUNK_PREFILL) : st;
 }
 
@@ -295,7 +297,7 @@ sa_status sparse_attn_prefill_union(const sa_attn_desc* desc, const void* q, con
   p.num_reqs = 1;
   if (legal == SA_OK_FALLBACK) {
     // G * group > 32: the per-token path gives every row its own result
-    st = launch_attention(kernel, p, 0, stream);
+    st = launch_attention(kernel, p, 2 * p.group <= 16 ? 3 : 0, stream);
     return st == SA_OK ? ok(SA_ENTRY_PREFILL_UNION, SA_OK_FALLBACK) : st;
   }
   UnionLayout L;

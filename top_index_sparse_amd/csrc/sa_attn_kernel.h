@@ -50,7 +50,11 @@
 
 namespace sa {
 
-enum : int { kPerToken = 0, kRagged = 1, kUnion = 2 };
+// kPaired / kPairedRagged: per-token results computed for two consecutive
+// rows per wavefront; each slot position either serves both rows (same
+// token) or is split, the second row's differing tokens being queued and
+// gathered as extra tiles.
+enum : int { kPerToken = 0, kRagged = 1, kUnion = 2, kPaired = 3, kPairedRagged = 4 };
 
 
 template <int DQK, int DV, bool V_IN_K, int MODE, int NBUF, int WSPLIT>
@@ -60,6 +64,9 @@ struct AttnTile {
   static constexpr int MTILES = DV / 16 / WSPLIT;    // this wave's 16-wide d blocks of O^T
   static_assert(DQK % (32 * WSPLIT) == 0 && DV % (128 * WSPLIT) == 0, "head dims");
   static constexpr bool UNION = MODE == kUnion;
+  static constexpr bool PAIRED = MODE == kPaired || MODE == kPairedRagged;
+  static constexpr bool OWN = UNION || PAIRED;      // per-slot ownership bits
+  static_assert(!PAIRED || NBUF == 1, "the pair queue reuses the data buffer");
   // V inside the latent K row: the wave's K slice is its V columns
   // [split*MAIN, +MAIN) plus its rope columns [DV + split*ROPE, +ROPE), so V
   // is part of the one gathered slice and both operands are read from LDS.
@@ -79,7 +86,8 @@ struct AttnTile {
 
   struct Idx {
     int xk;          // index of slot m; lanes 4g+i hold those of slots 4g+i
-    uint32_t bk;     // ownership bits of slot m (union)
+    uint32_t bk;     // ownership bits of slot m (union, paired)
+    int xb;          // paired: the second row's index at the same position
   };
   struct Data {
     u32x4_t kd[KSTEPS];    // K operand rows (direct path) or raw 16-lane chunks (KLDS)
@@ -92,12 +100,14 @@ struct AttnTile {
 // `split` of WSPLIT. xch is the workgroup's exchange buffer [2][4][64].
 template <int DQK, int DV, bool V_IN_K, int MODE, int NBUF, int WSPLIT>
 __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int split,
-                                          f32x4_t (*xch)[64], uint8_t* klds) {
+                                          f32x4_t (*xch)[64], uint8_t* klds, int32_t* pqs) {
   using TT = AttnTile<DQK, DV, V_IN_K, MODE, NBUF, WSPLIT>;
   constexpr int KSTEPS = TT::KSTEPS;
   constexpr int VCH = TT::VCH;
   constexpr int MTILES = TT::MTILES;
   constexpr bool UNION = TT::UNION;
+  constexpr bool PAIRED = TT::PAIRED;
+  constexpr bool OWN = TT::OWN;
   constexpr bool KLDS = TT::KLDS;
   constexpr bool VKLDS = TT::VKLDS;
   constexpr int KCH = TT::KCH;
@@ -125,7 +135,52 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
   int jmax;
   int64_t kv_base = 0;
   int kv_len = p.kv_len;
-  if (UNION) {
+  // paired: the two rows' request bases, lengths, index rows and limits
+  int64_t base0 = 0, base1 = 0;
+  int len0 = p.kv_len, len1 = p.kv_len, jmax0 = 0, jmax1 = 0;
+  const int32_t* irow1 = nullptr;
+  if (PAIRED) {
+    const int pairs = (p.num_rows + 1) >> 1;
+    const int pairs4 = (pairs + 3) & ~3;
+    kvh = wave_id / pairs4;
+    const int pr = wave_id - kvh * pairs4;
+    if (pr >= pairs || kvh >= p.num_kv_heads) return;
+    const int t0 = 2 * pr;
+    const int rows = t0 + 1 < p.num_rows ? 2 : 1;
+    const int j = n / group;
+    col_live = n < rows * group;
+    head_col = kvh * group + (n - j * group);
+    t_col = t0 + (col_live ? j : 0);
+    col_bit = col_live ? (1u << j) : 0u;
+    wave_bits = rows == 2 ? 3u : 1u;
+    auto request = [&](int t, int64_t& base, int& len) {
+      int lo = 0, hi = p.num_reqs - 1;  // last request whose first row is <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      base = p.cu_kv[lo];
+      len = (int)(p.cu_kv[lo + 1] - base);
+    };
+    if (MODE == kPairedRagged) {
+      request(t0, base0, len0);
+      if (rows == 2) request(t0 + 1, base1, len1);
+    }
+    auto limit = [&](int t, int len) {
+      int jm = p.topk;
+      if (p.topk_len) {
+        const int tl = p.topk_len[t];
+        jm = tl < 0 ? 0 : (tl < jm ? tl : jm);
+      }
+      return len > 0 ? jm : 0;
+    };
+    jmax0 = limit(t0, len0);
+    jmax1 = rows == 2 ? limit(t0 + 1, len1) : 0;
+    irow = p.idx + (int64_t)t0 * p.idx_row_stride;
+    irow1 = irow + p.idx_row_stride;
+    jmax = jmax0 > jmax1 ? jmax0 : jmax1;
+    kv_len = 0x7fffffff;   // slots carry global token ids; -1 marks invalid
+  } else if (UNION) {
     const int per_head = p.num_groups * p.waves_per_group;
     kvh = wave_id / per_head;
     if (kvh >= p.num_kv_heads) return;
@@ -197,8 +252,30 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
   // cross-lane permute, which does not occupy the vector memory pipeline.
   auto load_idx = [&](Idx& ti, int j0) {
     const int jk = j0 + n;
-    ti.xk = jk < jmax ? irow[jk] : -1;
+    if (PAIRED) {
+      ti.xk = jk < jmax0 ? irow[jk] : -1;
+      ti.xb = jk < jmax1 ? irow1[jk] : -1;
+    } else {
+      ti.xk = jk < jmax ? irow[jk] : -1;
+    }
     if (UNION) ti.bk = jk < jmax ? (uint32_t)brow[jk] : 0u;
+  };
+
+  // Paired rows: position m serves both rows when they select the same
+  // token; otherwise the second row's token is queued (per wave, in LDS)
+  // and gathered later with other queued tokens as a tile of its own.
+  int32_t* pq = pqs + (threadIdx.x >> 6) * 32;
+  int qcount = 0;
+  auto resolve_pair = [&](Idx& ti) {
+    const int ga = (unsigned)ti.xk < (unsigned)len0 ? (int)(base0 + ti.xk) : -1;
+    const int gb = (unsigned)ti.xb < (unsigned)len1 ? (int)(base1 + ti.xb) : -1;
+    const bool same = ga >= 0 && ga == gb;
+    const bool diff = gb >= 0 && !same;
+    ti.xk = ga;
+    ti.bk = (ga >= 0 ? 1u : 0u) | (same ? 2u : 0u);
+    const uint32_t dm = (uint32_t)__ballot(diff) & 0xffffu;   // lanes 0..15 hold slots 0..15
+    if (g == 0 && diff) pq[qcount + __popc(dm & ((1u << n) - 1u))] = gb;
+    qcount += __popc(dm);
   };
 
   // Invalid slots skip their loads. Their K registers keep stale values
@@ -207,13 +284,13 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
   // which are multiplied by p = 0.
   auto load_data = [&](Data& td, const Idx& ti) {
     bool kok = (unsigned)ti.xk < (unsigned)kv_len;
-    if (UNION) kok = kok && (ti.bk & wave_bits);
+    if (OWN) kok = kok && (ti.bk & wave_bits);
     int xv[4];
     uint32_t bv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       xv[i] = __builtin_amdgcn_ds_bpermute((4 * g + i) << 2, ti.xk);
-      if (UNION) bv[i] = (uint32_t)__builtin_amdgcn_ds_bpermute((4 * g + i) << 2, (int)ti.bk);
+      if (OWN) bv[i] = (uint32_t)__builtin_amdgcn_ds_bpermute((4 * g + i) << 2, (int)ti.bk);
     }
     bool vok[4];
     uint32_t mask = 0;
@@ -221,7 +298,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
     for (int i = 0; i < 4; ++i) {
       bool ok = (unsigned)xv[i] < (unsigned)kv_len;
       bool mine = ok;
-      if (UNION) {
+      if (OWN) {
         ok = ok && (bv[i] & wave_bits);
         mine = ok && (bv[i] & col_bit);
       }
@@ -241,9 +318,9 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
         // cross-lane reads first, with every lane active (a permute under a
         // partial exec mask would read 0 from inactive source lanes)
         const int x = __builtin_amdgcn_ds_bpermute(slot << 2, ti.xk);
-        const uint32_t b = UNION ? (uint32_t)__builtin_amdgcn_ds_bpermute(slot << 2, (int)ti.bk) : 0u;
+        const uint32_t b = OWN ? (uint32_t)__builtin_amdgcn_ds_bpermute(slot << 2, (int)ti.bk) : 0u;
         bool ok = (unsigned)x < (unsigned)kv_len;
-        if (UNION) ok = ok && (b & wave_bits);
+        if (OWN) ok = ok && (b & wave_bits);
         const int d = ch < MAIN / 8 ? split * MAIN + 8 * ch : DV + split * ROPE + 8 * (ch - MAIN / 8);
         if (ok) td.kd[c] = ld16(kw + (int64_t)x * p.k_row_stride + d);
       }
@@ -367,6 +444,24 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
   constexpr int UNROLL = NBUF * NI;
   Idx ib[NI];
   Data db[NBUF];
+
+  // Gathers and consumes queued second-row tokens, 16 at a time (all of
+  // them when flushing). With one data buffer, the buffer is free here.
+  auto run_queue = [&](bool flush) {
+    while (qcount >= 16 || (flush && qcount > 0)) {
+      Idx si;
+      si.xk = n < qcount ? pq[n] : -1;
+      si.bk = 2u;
+      si.xb = -1;
+      load_data(db[0], si);
+      compute(db[0]);
+      const int rem = qcount > 16 ? qcount - 16 : 0;
+      const int v = n < rem ? pq[16 + n] : 0;
+      if (g == 0 && n < rem) pq[n] = v;
+      qcount = rem;
+    }
+  };
+
 #pragma unroll
   for (int u = 0; u < NBUF; ++u) {
 #pragma unroll
@@ -389,12 +484,16 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
       if (cur >= ntiles) break;
       if (cur + NBUF < ntiles) load_idx(ib[(u + NBUF) % NI], (cur + NBUF) * TILE);
       __builtin_amdgcn_sched_barrier(0);
-      if (cur + NBUF - 1 < ntiles)
+      if (cur + NBUF - 1 < ntiles) {
+        if (PAIRED) resolve_pair(ib[(u + NBUF - 1) % NI]);
         load_data(db[(u + NBUF - 1) % NBUF], ib[(u + NBUF - 1) % NI]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       compute(db[u % NBUF]);
+      if (PAIRED) run_queue(false);
     }
   }
+  if (PAIRED) run_queue(true);
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ---------------------
   float l = l_run + __shfl_xor(l_run, 16);
@@ -431,20 +530,25 @@ attn_kernel(AttnParams p) {
   using TT = AttnTile<DQK, DV, V_IN_K, MODE, NBUF, WSPLIT>;
   __shared__ f32x4_t xch[(WSPLIT > 1 ? 2 : 1) * TT::WG_WAVES][64];
   __shared__ __attribute__((aligned(16))) uint8_t klds[TT::WG_WAVES * TT::KLDS_BYTES];
+  __shared__ int32_t pqs[TT::PAIRED ? TT::WG_WAVES * 32 : 1];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (WSPLIT == 1)
-    attn_wave<DQK, DV, V_IN_K, MODE, NBUF, 1>(p, bid * 4 + w, 0, xch, klds);
+    attn_wave<DQK, DV, V_IN_K, MODE, NBUF, 1>(p, bid * 4 + w, 0, xch, klds, pqs);
   else
-    attn_wave<DQK, DV, V_IN_K, MODE, NBUF, WSPLIT>(p, bid, w, xch, klds);
+    attn_wave<DQK, DV, V_IN_K, MODE, NBUF, WSPLIT>(p, bid, w, xch, klds, pqs);
 }
 
 // Workgroups and threads per workgroup for a launch.
 template <int WSPLIT>
 inline void attn_grid(const AttnParams& p, int mode, dim3* grid, dim3* block) {
-  const int64_t vwaves = mode == kUnion
-      ? (int64_t)p.num_groups * p.waves_per_group * p.num_kv_heads
-      : (int64_t)((p.num_rows + 3) / 4) * 4 * p.num_kv_heads;
+  int64_t vwaves;
+  if (mode == kUnion)
+    vwaves = (int64_t)p.num_groups * p.waves_per_group * p.num_kv_heads;
+  else if (mode == kPaired || mode == kPairedRagged)
+    vwaves = (int64_t)((((p.num_rows + 1) >> 1) + 3) & ~3) * p.num_kv_heads;
+  else
+    vwaves = (int64_t)((p.num_rows + 3) / 4) * 4 * p.num_kv_heads;
   if (WSPLIT == 1) {
     *grid = dim3((unsigned)((vwaves + 3) / 4));
     *block = dim3(256);

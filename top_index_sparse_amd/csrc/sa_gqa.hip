@@ -30,6 +30,14 @@ hipError_t launch_attn_gqa256(const AttnParams& p, int mode, hipStream_t stream)
       hipLaunchKernelGGL((attn_kernel<256, 256, false, kRagged, kGqaNbuf, kGqaWsplit, kGqaWaves>),
                          grid, block, 0, stream, p);
       break;
+    case kPaired:
+      hipLaunchKernelGGL((attn_kernel<256, 256, false, kPaired, 1, kGqaWsplit, kGqaWaves>),
+                         grid, block, 0, stream, p);
+      break;
+    case kPairedRagged:
+      hipLaunchKernelGGL((attn_kernel<256, 256, false, kPairedRagged, 1, kGqaWsplit, kGqaWaves>),
+                         grid, block, 0, stream, p);
+      break;
     default:
       hipLaunchKernelGGL((attn_kernel<256, 256, false, kUnion, kGqaNbuf, kGqaWsplit, kGqaWaves>),
                          grid, block, 0, stream, p);

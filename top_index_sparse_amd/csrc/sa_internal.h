@@ -69,7 +69,8 @@ struct PageParams {
   int32_t scale_bytes;
 };
 
-// mode: 0 per-token, 1 ragged chunk prefill, 2 union
+// mode: 0 per-token, 1 ragged chunk prefill, 2 union, 3 per-token with
+// paired rows, 4 ragged with paired rows
 hipError_t launch_attn_gqa256(const AttnParams& p, int mode, hipStream_t stream);
 hipError_t launch_attn_mla576(const AttnParams& p, int mode, hipStream_t stream);
 hipError_t launch_union_build(const UnionBuildParams& p, hipStream_t stream);

@@ -31,6 +31,14 @@ hipError_t launch_attn_mla576(const AttnParams& p, int mode, hipStream_t stream)
       hipLaunchKernelGGL((attn_kernel<576, 512, true, kRagged, kMlaNbuf, kMlaWsplit, kMlaWaves>),
                          grid, block, 0, stream, p);
       break;
+    case kPaired:
+      hipLaunchKernelGGL((attn_kernel<576, 512, true, kPaired, 1, kMlaWsplit, kMlaWaves>),
+                         grid, block, 0, stream, p);
+      break;
+    case kPairedRagged:
+      hipLaunchKernelGGL((attn_kernel<576, 512, true, kPairedRagged, 1, kMlaWsplit, kMlaWaves>),
+                         grid, block, 0, stream, p);
+      break;
     default:
       hipLaunchKernelGGL((attn_kernel<576, 512, true, kUnion, kMlaNbuf, kMlaWsplit, kMlaWaves>),
                          grid, block, 0, stream, p);
