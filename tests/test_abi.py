@@ -76,6 +76,8 @@ def test_validate_ok_shapes():
     (dict(q_row_stride=6 * 256 + 4), -2),
     (dict(kv_row_stride=250), -2),
     (dict(v_row_stride=260), -2),
+    (dict(kv_row_stride=1 << 31), -2),
+    (dict(v_row_stride=1 << 31), -2),
     (dict(idx_row_stride=2050), -2),
     (dict(out_row_stride=6 * 256 + 2), -2),
 ])

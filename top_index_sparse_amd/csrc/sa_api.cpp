@@ -65,11 +65,13 @@ sa_status check_desc(const sa_attn_desc* d, int32_t G, Kernel* kernel) {
   if (d->q_row_stride < qrow || d->q_row_stride % 8)
     return fail(SA_ERR_SHAPE, "q_row_stride %lld: needs >= %lld and a multiple of 8",
                 (long long)d->q_row_stride, (long long)qrow);
-  if (d->kv_row_stride < krow || d->kv_row_stride % 8)
-    return fail(SA_ERR_SHAPE, "kv_row_stride %lld: needs >= %lld and a multiple of 8",
+  // Row byte strides are 32-bit multipliers in the kernels' address math.
+  if (d->kv_row_stride < krow || d->kv_row_stride % 8 || d->kv_row_stride >= (int64_t)1 << 31)
+    return fail(SA_ERR_SHAPE, "kv_row_stride %lld: needs >= %lld, a multiple of 8, < 2^31",
                 (long long)d->kv_row_stride, (long long)krow);
-  if (!d->v_in_k && (d->v_row_stride < vrow || d->v_row_stride % 8))
-    return fail(SA_ERR_SHAPE, "v_row_stride %lld: needs >= %lld and a multiple of 8",
+  if (!d->v_in_k &&
+      (d->v_row_stride < vrow || d->v_row_stride % 8 || d->v_row_stride >= (int64_t)1 << 31))
+    return fail(SA_ERR_SHAPE, "v_row_stride %lld: needs >= %lld, a multiple of 8, < 2^31",
                 (long long)d->v_row_stride, (long long)vrow);
   if (d->idx_row_stride < d->topk)
     return fail(SA_ERR_SHAPE, "idx_row_stride %lld < topk %d", (long long)d->idx_row_stride,

@@ -15,9 +15,14 @@
 // from global memory straight into the register where the matrix core wants
 // it, with no LDS and no barrier:
 //
+//   Slot indices: lane (g = l/16, m = l%16) loads the index of slot
+//     4g + (m & 3) and turns it into the slot's K and V row byte offsets
+//     (one 32 x 32 -> 64-bit multiply per stride for all 16 slots); a DPP
+//     quad broadcast hands slots 4g..4g+3 to all sixteen lanes of group g.
 //   S^T[slot, col] = K_tile(16 x DQK) . Q^T(DQK x 16)       mfma 16x16x32 bf16
-//     lane (g = l/16, m = l%16) loads K row of slot m at d = 32s + 8g
-//     (s < DQK/32): four lanes read 64 contiguous bytes per instruction.
+//     lane (g, m) loads the K rows of slots 4g+i at bytes 256h + 16m and
+//     writes them to a wave-private LDS tile, from which lane (g, m) reads
+//     slot m at d = 32s + 8g (the A operand).
 //   P^T = exp2(S^T - max): the S^T accumulator (lane (g, n) holds slots
 //     4g..4g+3 of column n) is already the B operand of the next product.
 //   O^T[d, col] += V^T(16 x 16 slots) . P^T(16 slots x 16)   mfma 16x16x16 bf16
@@ -28,7 +33,10 @@
 //     already holds, so V needs no transpose.
 //   All O^T accumulators of lane (g, n) belong to column n, whose running
 //   max and partial sum the lane holds after two cross-lane max steps per
-//   tile; the sum is accumulated from the unrounded fp32 probabilities.
+//   tile; the sum is accumulated from the unrounded fp32 probabilities. The
+//   reference max only moves when a score passes it by more than kSlack
+//   (log2 units), so the O^T rescale is rare; probabilities up to 2^kSlack
+//   are exact in fp32 and bf16 rounding is relative, so nothing is lost.
 //
 // With WSPLIT = 2 a 16-column tile is shared by two wavefronts: each
 // computes half of the S^T k-steps (the two partial accumulators are summed
@@ -56,6 +64,9 @@ namespace sa {
 // gathered as extra tiles.
 enum : int { kPerToken = 0, kRagged = 1, kUnion = 2, kPaired = 3, kPairedRagged = 4 };
 
+// Headroom of the running max in log2 units: probabilities stay <= 2^kSlack.
+constexpr float kSlack = 8.f;
+
 
 template <int DQK, int DV, bool V_IN_K, int MODE, int NBUF, int WSPLIT>
 struct AttnTile {
@@ -77,6 +88,8 @@ struct AttnTile {
   // K staged through LDS when this wave's K slice is a whole number of
   // 256-byte halves per slot (16 lanes x 16 B each).
   static constexpr bool KLDS = !VKLDS && KSTEPS % 4 == 0;
+  static_assert(KLDS || VKLDS, "K is staged through LDS");
+  static_assert(!V_IN_K || VKLDS, "V inside K is read from the staged K slice");
   static constexpr int KCH = KLDS ? KSTEPS / 4 : 0;   // 16-byte K chunks per slot per lane
   static constexpr int KROW = 64 * KSTEPS + 16;       // LDS row pitch (bytes): 16 (mod 32) * odd
   static constexpr int KLDS_BYTES = (KLDS || VKLDS) ? 16 * KROW : 16;
@@ -85,12 +98,12 @@ struct AttnTile {
   static constexpr int WG_WAVES = WSPLIT == 1 ? 4 : WSPLIT;
 
   struct Idx {
-    int xk;          // index of slot m; lanes 4g+i hold those of slots 4g+i
-    uint32_t bk;     // ownership bits of slot m (union, paired)
+    int xk;          // index of slot 4g + (m & 3) at lane (g, m)
+    uint32_t bk;     // its ownership bits (union, paired)
     int xb;          // paired: the second row's index at the same position
   };
   struct Data {
-    u32x4_t kd[KSTEPS];    // K operand rows (direct path) or raw 16-lane chunks (KLDS)
+    u32x4_t kd[KSTEPS];    // raw K chunks, staged through LDS before the MFMA
     u32x4_t vd[4 * VCH];   // vd[VCH*i + h]: slot 4g+i, d = 128h + 8m .. +7
     uint32_t vmask;        // bit i: slot 4g+i contributes to this lane's column
   };
@@ -108,7 +121,6 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
   constexpr bool UNION = TT::UNION;
   constexpr bool PAIRED = TT::PAIRED;
   constexpr bool OWN = TT::OWN;
-  constexpr bool KLDS = TT::KLDS;
   constexpr bool VKLDS = TT::VKLDS;
   constexpr int KCH = TT::KCH;
   constexpr int KROW = TT::KROW;
@@ -248,10 +260,11 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
   }
 
   // One index (and ownership byte) load per lane per tile: lane (g, m)
-  // reads slot m; the V slots 4g..4g+3 come from lanes 4g..4g+3 by a
-  // cross-lane permute, which does not occupy the vector memory pipeline.
+  // reads slot 4g + (m & 3), so each quad of lanes holds the four slots
+  // whose rows lane group g gathers.
+  const int own_slot = 4 * g + (n & 3);
   auto load_idx = [&](Idx& ti, int j0) {
-    const int jk = j0 + n;
+    const int jk = j0 + own_slot;
     if (PAIRED) {
       ti.xk = jk < jmax0 ? irow[jk] : -1;
       ti.xb = jk < jmax1 ? irow1[jk] : -1;
@@ -273,76 +286,73 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
     const bool diff = gb >= 0 && !same;
     ti.xk = ga;
     ti.bk = (ga >= 0 ? 1u : 0u) | (same ? 2u : 0u);
-    const uint32_t dm = (uint32_t)__ballot(diff) & 0xffffu;   // lanes 0..15 hold slots 0..15
-    if (g == 0 && diff) pq[qcount + __popc(dm & ((1u << n) - 1u))] = gb;
-    qcount += __popc(dm);
+    // one lane per slot: lanes (g, 0..3) hold slots 4g .. 4g+3
+    const uint64_t dm = (uint64_t)__ballot(diff) & 0x000f000f000f000full;
+    if (n < 4 && diff) pq[qcount + __popcll(dm & ((1ull << lane) - 1ull))] = gb;
+    qcount += __popcll(dm);
   };
 
   // Invalid slots skip their loads. Their K registers keep stale values
   // (their scores are forced to -inf), and their V registers keep stale
   // finite values from an earlier tile, or the zeros set before the loop,
   // which are multiplied by p = 0.
+  const uint32_t k_row_bytes = (uint32_t)(2 * p.k_row_stride);   // < 2^32 (host check)
+  const uint32_t v_row_bytes = (uint32_t)(2 * p.v_row_stride);
+  const uint8_t* kwb = reinterpret_cast<const uint8_t*>(kw);
+  const uint8_t* kbn = kwb + 16 * n;   // this lane's 16 bytes of a 256-byte half row
+  const uint8_t* vbn = reinterpret_cast<const uint8_t*>(vw) + 16 * n;
   auto load_data = [&](Data& td, const Idx& ti) {
-    bool kok = (unsigned)ti.xk < (unsigned)kv_len;
-    if (OWN) kok = kok && (ti.bk & wave_bits);
-    int xv[4];
-    uint32_t bv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xv[i] = __builtin_amdgcn_ds_bpermute((4 * g + i) << 2, ti.xk);
-      if (OWN) bv[i] = (uint32_t)__builtin_amdgcn_ds_bpermute((4 * g + i) << 2, (int)ti.bk);
-    }
-    bool vok[4];
+    // Byte offsets of this lane's slot rows; -1 when no row of this wave
+    // uses the slot.
+    bool ok = (unsigned)ti.xk < (unsigned)kv_len;
+    if (OWN) ok = ok && (ti.bk & wave_bits);
+    const int64_t koff = ok ? (int64_t)((uint64_t)(uint32_t)ti.xk * k_row_bytes) : -1;
+    int khi[4];
+    quad_bcast4((int)(koff >> 32), khi);
     uint32_t mask = 0;
+    if (OWN) {
+      int bq[4];
+      quad_bcast4((int)ti.bk, bq);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bool ok = (unsigned)xv[i] < (unsigned)kv_len;
-      bool mine = ok;
-      if (OWN) {
-        ok = ok && (bv[i] & wave_bits);
-        mine = ok && (bv[i] & col_bit);
-      }
-      vok[i] = ok;
-      mask |= (uint32_t)mine << i;
+      for (int i = 0; i < 4; ++i) mask |= (uint32_t)(khi[i] >= 0 && ((uint32_t)bq[i] & col_bit)) << i;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mask |= (uint32_t)(khi[i] >= 0) << i;
     }
-    td.vmask = mask;
+    td.vmask = mask;   // bit i: slot 4g+i contributes to this lane's column
     if (VKLDS) {
       // Linear chunk order: load c covers chunks 64c .. 64c+63 of the tile's
       // 16 slot rows (CPR chunks each), so consecutive lanes read
-      // consecutive 16-byte pieces of the same row.
+      // consecutive 16-byte pieces of the same row. Slot s's offset sits in
+      // lane 16(s/4) + s%4; the permutes run with every lane active.
 #pragma unroll
       for (int c = 0; c < KSTEPS; ++c) {
         const int q = 64 * c + lane;
         const int slot = q / CPR;
         const int ch = q - slot * CPR;
-        // cross-lane reads first, with every lane active (a permute under a
-        // partial exec mask would read 0 from inactive source lanes)
-        const int x = __builtin_amdgcn_ds_bpermute(slot << 2, ti.xk);
-        const uint32_t b = OWN ? (uint32_t)__builtin_amdgcn_ds_bpermute(slot << 2, (int)ti.bk) : 0u;
-        bool ok = (unsigned)x < (unsigned)kv_len;
-        if (OWN) ok = ok && (b & wave_bits);
+        const int src = (16 * (slot >> 2) + (slot & 3)) << 2;
+        const int lo = __builtin_amdgcn_ds_bpermute(src, (int)koff);
+        const int hi = __builtin_amdgcn_ds_bpermute(src, (int)(koff >> 32));
         const int d = ch < MAIN / 8 ? split * MAIN + 8 * ch : DV + split * ROPE + 8 * (ch - MAIN / 8);
-        if (ok) td.kd[c] = ld16(kw + (int64_t)x * p.k_row_stride + d);
+        if (hi >= 0) td.kd[c] = ld16(kwb + join64(lo, hi) + 2 * d);
       }
       return;
     }
-    if (!KLDS && kok) {
-      const uint16_t* kp = kw + (int64_t)ti.xk * p.k_row_stride + 8 * g;
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) td.kd[s] = ld16(kp + 32 * s);
-    }
+    const int64_t voff = ok ? (int64_t)((uint64_t)(uint32_t)ti.xk * v_row_bytes) : -1;
+    int klo[4], vlo[4], vhi[4];
+    quad_bcast4((int)koff, klo);
+    quad_bcast4((int)voff, vlo);
+    quad_bcast4((int)(voff >> 32), vhi);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (vok[i]) {
-        if (KLDS) {
-          // K row of slot 4g+i, bytes 256h + 16m: sixteen lanes per row
-          const uint16_t* kp = kw + (int64_t)xv[i] * p.k_row_stride + 8 * n;
+      if (khi[i] >= 0) {
+        // K and V rows of slot 4g+i, bytes 256h + 16m: sixteen lanes per row
+        const uint8_t* kp = kbn + join64(klo[i], khi[i]);
 #pragma unroll
-          for (int h = 0; h < KCH; ++h) td.kd[KCH * i + h] = ld16(kp + 128 * h);
-        }
-        const uint16_t* vp = vw + (int64_t)xv[i] * p.v_row_stride + 8 * n;
+        for (int h = 0; h < KCH; ++h) td.kd[KCH * i + h] = ld16(kp + 256 * h);
+        const uint8_t* vp = vbn + join64(vlo[i], vhi[i]);
 #pragma unroll
-        for (int h = 0; h < VCH; ++h) td.vd[VCH * i + h] = ld16(vp + 128 * h);
+        for (int h = 0; h < VCH; ++h) td.vd[VCH * i + h] = ld16(vp + 256 * h);
       }
     }
   };
@@ -370,7 +380,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
         const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lk + n * KROW + 64 * s + 16 * g);
         st = mfma_16x16x32(a, qop[s], st);
       }
-    } else if (KLDS) {
+    } else {
       // Transpose the gathered K rows into the MFMA A layout through LDS:
       // write slot 4g+i, bytes 256h + 16m; read slot m, bytes 64s + 16g.
       // The pitch KROW = 16 (mod 256) keeps both sides bank-conflict free.
@@ -384,9 +394,6 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
         const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lk + n * KROW + 64 * s + 16 * g);
         st = mfma_16x16x32(a, qop[s], st);
       }
-    } else {
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) st = mfma_16x16x32(td.kd[s], qop[s], st);
     }
     if (WSPLIT > 1) {
       // partial S^T of the other half of d; both waves form half0 + half1
@@ -403,14 +410,16 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
     float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
+    const float m_cand = fmaxf(m_run, mx);
+    const float m_new = m_cand > m_run + kSlack ? m_cand : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
     float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s2[i] - m_use);
     l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    // Rescale only when some column's max moved (alpha == 1 elsewhere).
+    // Rescale only when some column's reference max moved (alpha == 1
+    // elsewhere).
     if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
 #pragma unroll
       for (int mt = 0; mt < MTILES; ++mt) acc[mt] *= alpha;
@@ -450,7 +459,7 @@ __device__ __forceinline__ void attn_wave(const AttnParams& p, int wave_id, int 
   auto run_queue = [&](bool flush) {
     while (qcount >= 16 || (flush && qcount > 0)) {
       Idx si;
-      si.xk = n < qcount ? pq[n] : -1;
+      si.xk = own_slot < qcount ? pq[own_slot] : -1;
       si.bk = 2u;
       si.xb = -1;
       load_data(db[0], si);

@@ -37,19 +37,34 @@ __device__ __forceinline__ uint32_t bf16_elem(u32x4_t v, int e) {
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-// Pack element e of four chunks into the 4 x bf16 operand of a K=16 MFMA.
+// Pack element e of four chunks into the 4 x bf16 operand of a K=16 MFMA:
+// one byte permute per output register (v_perm_b32 picks bytes 0-3 from its
+// second source and 4-7 from its first).
 __device__ __forceinline__ i16x4_t gather_col4(u32x4_t c0, u32x4_t c1, u32x4_t c2, u32x4_t c3,
                                                int e) {
-  const uint32_t w0 = c0[e >> 1], w1 = c1[e >> 1], w2 = c2[e >> 1], w3 = c3[e >> 1];
-  uint32_t lo, hi;
-  if (e & 1) {
-    lo = (w0 >> 16) | (w1 & 0xffff0000u);
-    hi = (w2 >> 16) | (w3 & 0xffff0000u);
-  } else {
-    lo = (w0 & 0xffffu) | (w1 << 16);
-    hi = (w2 & 0xffffu) | (w3 << 16);
-  }
+  const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+  const uint32_t lo = __builtin_amdgcn_perm(c1[e >> 1], c0[e >> 1], sel);
+  const uint32_t hi = __builtin_amdgcn_perm(c3[e >> 1], c2[e >> 1], sel);
   return __builtin_bit_cast(i16x4_t, (u32x2_t){lo, hi});
+}
+
+// Lane 4q+I's value in every lane of quad q (DPP quad_perm [I, I, I, I]);
+// all lanes must be active.
+template <int I>
+__device__ __forceinline__ int quad_bcast(int v) {
+  return __builtin_amdgcn_mov_dpp(v, I * 0x55, 0xf, 0xf, false);
+}
+
+// 64-bit value from its two halves (a register pair, no arithmetic).
+__device__ __forceinline__ uint64_t join64(int lo, int hi) {
+  return __builtin_bit_cast(uint64_t, (u32x2_t){(uint32_t)lo, (uint32_t)hi});
+}
+
+__device__ __forceinline__ void quad_bcast4(int v, int out[4]) {
+  out[0] = quad_bcast<0>(v);
+  out[1] = quad_bcast<1>(v);
+  out[2] = quad_bcast<2>(v);
+  out[3] = quad_bcast<3>(v);
 }
 
 // D = A(16x32) * B(32x16) + C; lane l holds A row l%16, B column l%16, each
