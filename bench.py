@@ -158,6 +158,8 @@ def measure_others(args, sa, torch, stream):
     out = torch.empty((c.num_rows, c.num_q_heads, 256), dtype=torch.float32, device="cuda")
     lse = torch.empty((c.num_rows, c.num_q_heads), dtype=torch.float32, device="cuda")
     per_token_bytes = gathered_bytes(c)
+    cu_q1 = torch.tensor([0, c.num_rows], dtype=torch.int32, device="cuda")
+    cu_kv1 = torch.tensor([0, c.kv_len], dtype=torch.int64, device="cuda")
     ws = torch.empty(sa.sparse_attn_union_workspace_bytes(c.num_rows, c.topk, 2),
                      dtype=torch.uint8, device="cuda")
     ui, ub, ul = sa.sparse_attn_union_build(idx, c.kv_len, 2, ws=ws, stream=stream)
@@ -172,7 +174,19 @@ def measure_others(args, sa, torch, stream):
               "attention_ms": round(ms_all - ms_build, 4),
               "per_token_equivalent_GBps": round(per_token_bytes / (ms_all * 1e-3) / 1e9, 1)})
     res["gqa_union_G2_same_workload"] = r
-    del q, k, v, idx, out, lse, ws, ui, ub, ul
+    # The same sets with each row's slot order shuffled: the walk keeps
+    # shared tokens at the same slot position in adjacent rows, which the
+    # per-token path's row pairing uses; without that alignment the pairing
+    # only queues, and the union path (which sorts) keeps its sharing.
+    sidx = torch.from_numpy(gen.shuffle_slots(c.idx, args.seed + 1)).cuda()
+    ms = _events_ms(torch, stream, lambda: sa.sparse_attn_chunk_prefill(
+        q, k, v, sidx, cu_q1, cu_kv1, sm_scale=c.scale, out=out, lse=lse, stream=stream), w, n)
+    r = _rate(per_token_bytes, ms)
+    ms_u = _events_ms(torch, stream, lambda: sa.sparse_attn_prefill_union(
+        q, k, v, sidx, 2, sm_scale=c.scale, ws=ws, out=out, lse=lse, stream=stream), w, n)
+    r.update({"union_G2_ms": round(ms_u, 4)})
+    res["shuffled_slots_same_sets"] = r
+    del q, k, v, idx, sidx, out, lse, ws, ui, ub, ul
 
     # group 12 over two KV heads, 131072-token context
     c = gen.make_config("C2", args.seed)

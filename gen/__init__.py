@@ -203,6 +203,16 @@ class AttnCase:
         return d
 
 
+def shuffle_slots(idx: np.ndarray, seed: int) -> np.ndarray:
+    """The same index sets with every row's slot order permuted at random.
+
+    The walk keeps a surviving token at its slot position from one row to the
+    next; this variant removes that alignment while keeping each row's set,
+    its padding and the overlap between rows.
+    """
+    return np.random.default_rng(seed).permuted(idx, axis=1)
+
+
 def make_attn_case(name: str, *, seed: int, num_rows: int, kv_len: int,
                    first_pos: int, num_q_heads: int, num_kv_heads: int,
                    head_dim_qk: int, head_dim_v: int, topk: int,

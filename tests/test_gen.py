@@ -108,3 +108,13 @@ def test_page_case():
     for a in range(32):
         for b in range(a + 1, 32):
             assert not (per_req[a] & per_req[b])
+
+
+def test_shuffle_slots_keeps_sets_and_breaks_alignment():
+    rng = np.random.default_rng(4)
+    idx = gen.random_walk_indices(rng, np.arange(3000, 3064), 300)
+    sh = gen.shuffle_slots(idx, 9)
+    assert np.array_equal(np.sort(sh, axis=1), np.sort(idx, axis=1))
+    same_pos = (idx[1:] == idx[:-1]).mean()
+    assert same_pos > 0.9                      # the walk keeps slot positions
+    assert (sh[1:] == sh[:-1]).mean() < 0.05   # the shuffle does not

@@ -198,7 +198,8 @@ def test_union_fallback_when_tile_illegal():
     assert torch.equal(out, po) and torch.equal(lse, pl)
 
 
-@pytest.mark.parametrize("Hq,Hkv,G", [(6, 1, 2), (12, 2, 2), (4, 1, 4), (2, 1, 8), (6, 1, 5), (12, 1, 4)])
+@pytest.mark.parametrize("Hq,Hkv,G", [(6, 1, 2), (12, 2, 2), (4, 1, 4), (2, 1, 8), (6, 1, 5), (12, 1, 4),
+                                     (8, 1, 4), (12, 1, 2)])
 def test_union_gqa(Hq, Hkv, G):
     say(f"[union] GQA d=256 group {Hq // Hkv} x {Hkv} KV heads, G={G}")
     case = gen.make_attn_case("u", seed=35 + G, num_rows=23, kv_len=3000, first_pos=2977,

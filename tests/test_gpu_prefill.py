@@ -250,3 +250,42 @@ def test_paired_rows_with_disjoint_positions():
                                           sm_scale=case.scale)
     torch.cuda.synchronize()
     check_close(o2, l2, ro, rl, "paired ragged")
+
+
+@pytest.mark.parametrize("Hq", [6, 3, 12, 16])
+def test_team_rows_position_sharing(Hq):
+    # Teams of consecutive rows share slot positions: 16 / group rows for
+    # group <= 8, up to four rows over three 16-column tiles above that.
+    say(f"[prefill] team rows, group {Hq}: runs, gaps, realignments, straddled requests")
+    case = _small(17, 24, 1500, 1400, Hq, 1, 160)
+    idx = case.idx.copy()
+    rng = np.random.default_rng(8)
+    fresh = lambda k: rng.choice(np.arange(1400), size=k, replace=False).astype(np.int32)
+    idx[1] = idx[0]
+    idx[1, 5:35] = fresh(30)                       # a run of new tokens over rows 1-2
+    idx[2] = idx[1]
+    idx[3] = idx[0]                                # back to row 0
+    idx[5] = np.roll(idx[4], 3)                    # no position matches
+    idx[6] = idx[5]
+    idx[6, :20] = idx[4, :20]                      # partial realignment with row 4
+    idx[7] = idx[4]
+    idx[7, 40:60] = idx[4, 40]                     # duplicates of a shared token
+    idx[8] = -1                                    # empty first row
+    idx[9] = idx[10] = idx[11] = fresh(160)        # a run that row 0 does not share
+    idx[13] = idx[15] = idx[12]
+    idx[14] = fresh(160)                           # alternating sets A B A
+    idx[17, 80:] = -1                              # short rows inside a team
+    idx[18, ::3] = -1
+    case.idx = idx
+    dev = attn_to_dev(case)
+    out, lse = _run_prefill(case, dev)
+    ro, rl = _oracle(case)
+    check_close(out, lse, ro, rl, f"team rows group {Hq}")
+    cu_q = i32_dev(np.array([0, 5, 5, 13, 24]))    # teams that straddle requests
+    cu_kv = i64_dev(np.array([0, 1500, 1500, 3000, 4500]))
+    k3 = torch.cat([dev["k"]] * 3)
+    v3 = torch.cat([dev["v"]] * 3)
+    o2, l2 = sa.sparse_attn_chunk_prefill(dev["q"], k3, v3, dev["idx"], cu_q, cu_kv,
+                                          sm_scale=case.scale)
+    torch.cuda.synchronize()
+    check_close(o2, l2, ro, rl, f"team rows ragged group {Hq}")

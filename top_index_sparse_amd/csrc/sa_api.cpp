@@ -118,14 +118,15 @@ sa::AttnParams make_params(const sa_attn_desc* d, const void* q, const void* k, 
   return p;
 }
 
-sa_status launch_attention(Kernel kernel, const sa::AttnParams& p, int mode, hipStream_t s) {
+// union_mode: 0 per-token results (ragged when p.cu_q is set), 1 union lists
+sa_status launch_attention(Kernel kernel, const sa::AttnParams& p, int union_mode, hipStream_t s) {
   hipError_t e = hipSuccess;
   switch (kernel) {
     case Kernel::kGqa256:
-      e = sa::launch_attn_gqa256(p, mode, s);
+      e = sa::launch_attn_gqa256(p, union_mode, s);
       break;
     case Kernel::kMla576:
-      e = sa::launch_attn_mla576(p, mode, s);
+      e = sa::launch_attn_mla576(p, union_mode, s);
       break;
     default:
       return fail(SA_ERR_UNSUPPORTED, "no kernel for this head-dim combination");
@@ -214,9 +215,7 @@ sa_status sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const voi
   p.topk_len = topk_len;
   p.kv_len = kv_len;
   p.num_reqs = 1;
-  // Two rows per wavefront share the gathers of their common slots when
-  // both rows' heads fit one 16-column tile.
-  st = launch_attention(kernel, p, 2 * p.group <= 16 ? 3 : 0, stream);
+  st = launch_attention(kernel, p, 0, stream);
   return st == SA_OK ? ok(SA_ENTRY_PREFILL) : st;
 }
 
@@ -242,7 +241,7 @@ sa_status sparse_attn_chunk_prefill(const sa_attn_desc* desc, const void* q, con
   p.cu_q = cu_seqlens_q;
   p.cu_kv = cu_seqlens_kv;
   p.num_reqs = num_reqs;
-  st = launch_attention(kernel, p, 2 * p.group <= 16 ? 4 : 1, stream);
+  st = launch_attention(kernel, p, 0, stream);
   return st == SA_OK ? ok(SA_ENTRY_CHUNK_PREFILL) : st;
 }
 
@@ -299,7 +298,7 @@ sa_status sparse_attn_prefill_union(const sa_attn_desc* desc, const void* q, con
   p.num_reqs = 1;
   if (legal == SA_OK_FALLBACK) {
     // G * group > 32: the per-token path gives every row its own result
-    st = launch_attention(kernel, p, 2 * p.group <= 16 ? 3 : 0, stream);
+    st = launch_attention(kernel, p, 0, stream);
     return st == SA_OK ? ok(SA_ENTRY_PREFILL_UNION, SA_OK_FALLBACK) : st;
   }
   UnionLayout L;
@@ -324,9 +323,7 @@ sa_status sparse_attn_prefill_union(const sa_attn_desc* desc, const void* q, con
   p.union_stride = L.stride;
   p.G = G;
   p.num_groups = (int32_t)L.groups;
-  p.tokens_per_wave = 16 / p.group < G ? 16 / p.group : G;
-  p.waves_per_group = (G + p.tokens_per_wave - 1) / p.tokens_per_wave;
-  st = launch_attention(kernel, p, 2, stream);
+  st = launch_attention(kernel, p, 1, stream);
   return st == SA_OK ? ok(SA_ENTRY_PREFILL_UNION) : st;
 }
 

@@ -55,6 +55,20 @@ __device__ __forceinline__ int quad_bcast(int v) {
   return __builtin_amdgcn_mov_dpp(v, I * 0x55, 0xf, 0xf, false);
 }
 
+// Lane L's value in every lane of its row of 16 (DPP row_newbcast:L).
+template <int L>
+__device__ __forceinline__ int row_bcast(int v) {
+  return __builtin_amdgcn_mov_dpp(v, 0x150 + L, 0xf, 0xf, false);
+}
+
+// The values of lanes 0, 4, 8, 12 of each row of 16.
+__device__ __forceinline__ void row_bcast4(int v, int out[4]) {
+  out[0] = row_bcast<0>(v);
+  out[1] = row_bcast<4>(v);
+  out[2] = row_bcast<8>(v);
+  out[3] = row_bcast<12>(v);
+}
+
 // 64-bit value from its two halves (a register pair, no arithmetic).
 __device__ __forceinline__ uint64_t join64(int lo, int hi) {
   return __builtin_bit_cast(uint64_t, (u32x2_t){(uint32_t)lo, (uint32_t)hi});

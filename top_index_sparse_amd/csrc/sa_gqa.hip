@@ -1,47 +1,47 @@
 // Sparse GQA prefill kernels, head dim 256 (K and V separate, group <= 16):
-// per-token, ragged chunk prefill and union instantiations of attn_kernel.
+// per-token (one request or ragged requests) and union instantiations of
+// attn_kernel, for three team shapes.
 #include "sa_attn_kernel.h"
-
-#ifndef SA_GQA_NBUF
-#define SA_GQA_NBUF 1
-#endif
-#ifndef SA_GQA_WAVES
-#define SA_GQA_WAVES 2
-#endif
-#ifndef SA_GQA_WSPLIT
-#define SA_GQA_WSPLIT 1
-#endif
 
 namespace sa {
 
-constexpr int kGqaNbuf = SA_GQA_NBUF;      // K/V tiles in flight per wavefront
-constexpr int kGqaWaves = SA_GQA_WAVES;    // wavefronts per SIMD the registers allow
-constexpr int kGqaWsplit = SA_GQA_WSPLIT;  // wavefronts sharing one 16-column tile
+namespace {
 
-hipError_t launch_attn_gqa256(const AttnParams& p, int mode, hipStream_t stream) {
+template <int MODE, int C, int WSPLIT>
+void launch(const AttnParams& p, hipStream_t stream) {
   dim3 grid, block;
-  attn_grid<kGqaWsplit>(p, mode, &grid, &block);
-  switch (mode) {
-    case kPerToken:
-      hipLaunchKernelGGL((attn_kernel<256, 256, false, kPerToken, kGqaNbuf, kGqaWsplit, kGqaWaves>),
-                         grid, block, 0, stream, p);
-      break;
-    case kRagged:
-      hipLaunchKernelGGL((attn_kernel<256, 256, false, kRagged, kGqaNbuf, kGqaWsplit, kGqaWaves>),
-                         grid, block, 0, stream, p);
-      break;
-    case kPaired:
-      hipLaunchKernelGGL((attn_kernel<256, 256, false, kPaired, 1, kGqaWsplit, kGqaWaves>),
-                         grid, block, 0, stream, p);
-      break;
-    case kPairedRagged:
-      hipLaunchKernelGGL((attn_kernel<256, 256, false, kPairedRagged, 1, kGqaWsplit, kGqaWaves>),
-                         grid, block, 0, stream, p);
-      break;
-    default:
-      hipLaunchKernelGGL((attn_kernel<256, 256, false, kUnion, kGqaNbuf, kGqaWsplit, kGqaWaves>),
-                         grid, block, 0, stream, p);
-      break;
+  attn_grid<WSPLIT>(p, MODE, &grid, &block);
+  hipLaunchKernelGGL((attn_kernel<256, 256, false, MODE, C, WSPLIT, 2>), grid, block, 0, stream, p);
+}
+
+// One wave with whole K/V rows for 16 columns; two waves, each with half of
+// d, for 32 or 48 columns (union teams have at most 32).
+template <int MODE>
+void launch_cols(const AttnParams& p, int cols, hipStream_t stream) {
+  if (cols <= 16)
+    launch<MODE, 1, 1>(p, stream);
+  else if (MODE == kUnion || cols <= 32)
+    launch<MODE, 2, 2>(p, stream);
+  else
+    launch<kRows, 3, 2>(p, stream);
+}
+
+}  // namespace
+
+// Team shapes. Per-token: a team serves the consecutive rows that share its
+// gathered slot positions: 16 / group rows on one wave for group <= 8 (the
+// wave's 16 columns), up to four rows on two waves with three 16-column
+// tiles above that. Union: one team per group (G x group <= 32 columns by
+// the host).
+hipError_t launch_attn_gqa256(AttnParams p, int union_mode, hipStream_t stream) {
+  if (union_mode) {
+    p.rows_per_team = p.G;
+    p.teams_per_group = 1;
+    launch_cols<kUnion>(p, p.G * p.group, stream);
+  } else {
+    const int r = p.group <= 8 ? 16 / p.group : 48 / p.group;
+    p.rows_per_team = r < 4 ? r : 4;
+    launch_cols<kRows>(p, p.rows_per_team * p.group, stream);
   }
   return hipGetLastError();
 }

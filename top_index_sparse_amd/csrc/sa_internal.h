@@ -37,8 +37,9 @@ struct AttnParams {
   int64_t union_stride;
   int32_t G;
   int32_t num_groups;
-  int32_t tokens_per_wave;    // rows of a group one wavefront serves
-  int32_t waves_per_group;
+  int32_t teams_per_group;    // union: teams serving one group
+  // rows one team serves (per-token: consecutive rows; union: group members)
+  int32_t rows_per_team;
 };
 
 struct UnionBuildParams {
@@ -69,10 +70,10 @@ struct PageParams {
   int32_t scale_bytes;
 };
 
-// mode: 0 per-token, 1 ragged chunk prefill, 2 union, 3 per-token with
-// paired rows, 4 ragged with paired rows
-hipError_t launch_attn_gqa256(const AttnParams& p, int mode, hipStream_t stream);
-hipError_t launch_attn_mla576(const AttnParams& p, int mode, hipStream_t stream);
+// union: 0 per-token results (ragged when cu_q is set), 1 union lists. The
+// launchers choose the team shape (rows per team, column tiles).
+hipError_t launch_attn_gqa256(AttnParams p, int union_mode, hipStream_t stream);
+hipError_t launch_attn_mla576(AttnParams p, int union_mode, hipStream_t stream);
 hipError_t launch_union_build(const UnionBuildParams& p, hipStream_t stream);
 hipError_t launch_page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src_pages,
                             int32_t src_page_tokens, int8_t* mask, hipStream_t stream);

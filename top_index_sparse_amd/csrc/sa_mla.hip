@@ -1,48 +1,24 @@
 // Sparse MLA prefill kernels: 576-wide latent rows (512 latent + 64 rope)
 // whose first 512 columns serve as V, group <= 16 query heads per latent
-// row: per-token, ragged and union instantiations of attn_kernel.
+// row: per-token (one request or ragged requests) and union instantiations
+// of attn_kernel. A team is one 16-column tile on two wavefronts (each half
+// of the latent columns), which keeps a wave's registers within budget.
 #include "sa_attn_kernel.h"
-
-#ifndef SA_MLA_NBUF
-#define SA_MLA_NBUF 1
-#endif
-#ifndef SA_MLA_WAVES
-#define SA_MLA_WAVES 2
-#endif
-#ifndef SA_MLA_WSPLIT
-#define SA_MLA_WSPLIT 2
-#endif
 
 namespace sa {
 
-constexpr int kMlaNbuf = SA_MLA_NBUF;      // K/V tiles in flight per wavefront
-constexpr int kMlaWaves = SA_MLA_WAVES;    // wavefronts per SIMD the registers allow
-constexpr int kMlaWsplit = SA_MLA_WSPLIT;  // wavefronts sharing one 16-column tile
-
-hipError_t launch_attn_mla576(const AttnParams& p, int mode, hipStream_t stream) {
+hipError_t launch_attn_mla576(AttnParams p, int union_mode, hipStream_t stream) {
   dim3 grid, block;
-  attn_grid<kMlaWsplit>(p, mode, &grid, &block);
-  switch (mode) {
-    case kPerToken:
-      hipLaunchKernelGGL((attn_kernel<576, 512, true, kPerToken, kMlaNbuf, kMlaWsplit, kMlaWaves>),
-                         grid, block, 0, stream, p);
-      break;
-    case kRagged:
-      hipLaunchKernelGGL((attn_kernel<576, 512, true, kRagged, kMlaNbuf, kMlaWsplit, kMlaWaves>),
-                         grid, block, 0, stream, p);
-      break;
-    case kPaired:
-      hipLaunchKernelGGL((attn_kernel<576, 512, true, kPaired, 1, kMlaWsplit, kMlaWaves>),
-                         grid, block, 0, stream, p);
-      break;
-    case kPairedRagged:
-      hipLaunchKernelGGL((attn_kernel<576, 512, true, kPairedRagged, 1, kMlaWsplit, kMlaWaves>),
-                         grid, block, 0, stream, p);
-      break;
-    default:
-      hipLaunchKernelGGL((attn_kernel<576, 512, true, kUnion, kMlaNbuf, kMlaWsplit, kMlaWaves>),
-                         grid, block, 0, stream, p);
-      break;
+  const int r = 16 / p.group;   // rows of one 16-column tile
+  if (union_mode) {
+    p.rows_per_team = r < p.G ? r : p.G;
+    p.teams_per_group = (p.G + p.rows_per_team - 1) / p.rows_per_team;
+    attn_grid<2>(p, kUnion, &grid, &block);
+    hipLaunchKernelGGL((attn_kernel<576, 512, true, kUnion, 1, 2, 2>), grid, block, 0, stream, p);
+  } else {
+    p.rows_per_team = r < 4 ? r : 4;
+    attn_grid<2>(p, kRows, &grid, &block);
+    hipLaunchKernelGGL((attn_kernel<576, 512, true, kRows, 1, 2, 2>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
