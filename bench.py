@@ -114,10 +114,11 @@ def cpu_baseline(case: gen.AttnCase, stride: int, workers: int):
     out_rows = np.concatenate([p[0] for p in parts])
     out_o = np.concatenate([p[1] for p in parts])
     out_l = np.concatenate([p[2] for p in parts])
+    which = "every row" if stride == 1 else f"every {stride}-th row"
     return {"value": nbytes / wall / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
-            "sample": f"every {stride}th row of the same workload ({len(rows)} of "
-                      f"{case.num_rows} rows, {nbytes / 1e9:.3f} GB gathered), fp64 numpy, "
-                      f"{workers} processes x 1 BLAS thread, {wall:.2f} s wall"}, \
+            "sample": f"{which} of the same workload ({len(rows)} of {case.num_rows} rows, "
+                      f"{nbytes / 1e9:.3f} GB gathered), fp64 numpy, {workers} processes x 1 "
+                      f"BLAS thread, {wall:.2f} s wall ({wall * workers:.0f} core-seconds)"}, \
         (out_rows, out_o, out_l)
 
 
@@ -280,7 +281,7 @@ def main():
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on",
                     help="off for profiler runs (the profiler initialises the GPU before "
                          "the program, so no worker processes may be forked)")
-    ap.add_argument("--cpu-stride", type=int, default=2)
+    ap.add_argument("--cpu-stride", type=int, default=1)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters)")
     ap.add_argument("--others", choices=["on", "off"], default="on",
