@@ -77,8 +77,14 @@ def _check_union_exact(idx_np, kv_len, G, groups=None):
     return ri, rb, rl
 
 
+# Bit planes in LDS while G x kv_len <= 2^19 (64 KB), sort and merge above:
+# (6, 500, 262144, 2) is the largest bitmap case, the next kv_len and the
+# last three rows take the sort path.
 @pytest.mark.parametrize("T,k,kv,G", [(9, 8, 20, 2), (10, 6, 12, 4), (7, 5, 9, 3), (5, 7, 30, 1),
-                                      (33, 100, 500, 8), (17, 2051, 40000, 2), (1, 1, 3, 4)])
+                                      (33, 100, 500, 8), (17, 2051, 40000, 2), (1, 1, 3, 4),
+                                      (6, 500, 262144, 2), (6, 500, 262145, 2),
+                                      (9, 300, 600000, 2), (12, 40, 70000, 8),
+                                      (20, 2051, 300000, 2)])
 def test_union_build_random_exact(T, k, kv, G):
     say(f"[union build] random T={T} k={k} kv={kv} G={G}")
     rng = np.random.default_rng(T * 1000 + k)

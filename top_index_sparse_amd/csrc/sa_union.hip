@@ -12,6 +12,16 @@
 // union_idx[g][r]; union_len[g] counts the listed indices.
 //
 // gfx950 design.
+//   Bitmap (when the group's planes fit 64 KB of LDS, G x kv_len <= 2^19):
+//   one workgroup per group keeps one bit plane per member over [0, kv_len)
+//   in LDS, marks each member's valid indices with atomic ORs, then scans
+//   the words in order. A token belongs to the bucket of its lowest owning
+//   member; each thread counts its word range per bucket, a block-wide scan
+//   turns the counts into output positions, and a second pass over the same
+//   words writes every token ascending within its bucket, with the OR of
+//   the planes as its bits. That is the output layout below, reached with
+//   O(G k + G kv_len / 32) work and no sort.
+//   Otherwise, sort and merge:
 //   Sort: one wavefront per row holds the row's N = 64R keys in registers
 //   (lane l owns keys lR .. lR+R-1). A bitonic network runs its
 //   compare-exchanges between registers of one lane when the partner
@@ -216,6 +226,110 @@ __global__ void __launch_bounds__(kMergeThreads) union_merge_kernel(UnionBuildPa
   if (threadIdx.x == 0) p.union_len[gi] = len;
 }
 
+constexpr int kBitmapThreads = 256;
+constexpr int kMaxMembers = 8;
+
+__global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuildParams p) {
+  extern __shared__ uint32_t planes[];   // [members][W]
+  __shared__ int32_t wave_tot[kBitmapThreads / 64][kMaxMembers];
+  const int gi = blockIdx.x;
+  const int first = gi * p.G;
+  int members = p.num_rows - first;
+  if (members > p.G) members = p.G;
+  const int W = (p.kv_len + 31) >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  for (int i = tid; i < members * W; i += kBitmapThreads) planes[i] = 0u;
+  __syncthreads();
+  for (int j = 0; j < members; ++j) {
+    const int32_t* row = p.idx + (int64_t)(first + j) * p.idx_row_stride;
+    uint32_t* plane = planes + j * W;
+    for (int e = tid; e < p.topk; e += kBitmapThreads) {
+      const int32_t x = row[e];
+      if ((unsigned)x < (unsigned)p.kv_len) atomicOr(&plane[x >> 5], 1u << (x & 31));
+    }
+  }
+  __syncthreads();
+
+  // Each thread owns a contiguous range of words; count its tokens per bucket.
+  const int wpt = (W + kBitmapThreads - 1) / kBitmapThreads;
+  const int w0 = min(W, tid * wpt), w1 = min(W, w0 + wpt);
+  int cnt[kMaxMembers];
+#pragma unroll
+  for (int j = 0; j < kMaxMembers; ++j) cnt[j] = 0;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t seen = 0u;
+#pragma unroll
+    for (int j = 0; j < kMaxMembers; ++j) {
+      if (j < members) {
+        const uint32_t b = planes[j * W + w];
+        cnt[j] += __popc(b & ~seen);
+        seen |= b;
+      }
+    }
+  }
+  // Exclusive scan of the counts over threads (thread order = word order),
+  // per bucket; bucket j starts after all tokens of buckets < j.
+  int excl[kMaxMembers];
+#pragma unroll
+  for (int j = 0; j < kMaxMembers; ++j) {
+    int incl = cnt[j];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    excl[j] = incl - cnt[j];
+    if (lane == 63) wave_tot[wave][j] = incl;
+  }
+  __syncthreads();
+  int pos[kMaxMembers];
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxMembers; ++j) {
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kBitmapThreads / 64; ++w) {
+      const int t = wave_tot[w][j];
+      if (w < wave) before += t;
+      total += t;
+    }
+    pos[j] = base + before + excl[j];
+    base += total;
+  }
+  const int len = base;
+
+  int32_t* uidx = p.union_idx + (int64_t)gi * p.union_stride;
+  uint8_t* ubits = p.union_bits + (int64_t)gi * p.union_stride;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t b[kMaxMembers];
+#pragma unroll
+    for (int j = 0; j < kMaxMembers; ++j) b[j] = j < members ? planes[j * W + w] : 0u;
+    uint32_t seen = 0u;
+#pragma unroll
+    for (int j = 0; j < kMaxMembers; ++j) {
+      uint32_t fresh = b[j] & ~seen;
+      seen |= b[j];
+      while (fresh) {
+        const int bit = __builtin_ctz(fresh);
+        fresh &= fresh - 1u;
+        uint32_t own = 0u;
+#pragma unroll
+        for (int jj = 0; jj < kMaxMembers; ++jj) own |= ((b[jj] >> bit) & 1u) << jj;
+        uidx[pos[j]] = w * 32 + bit;
+        ubits[pos[j]] = (uint8_t)own;
+        ++pos[j];
+      }
+    }
+  }
+  const int64_t width = (int64_t)p.G * p.topk;
+  for (int64_t r = len + tid; r < width; r += kBitmapThreads) {
+    uidx[r] = -1;
+    ubits[r] = 0;
+  }
+  if (tid == 0) p.union_len[gi] = len;
+}
+
 template <int R>
 void launch_sort(const UnionBuildParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(union_sort_kernel<R>, dim3((unsigned)p.num_rows), dim3(64), 0, stream, p);
@@ -224,6 +338,12 @@ void launch_sort(const UnionBuildParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_union_build(const UnionBuildParams& p, hipStream_t stream) {
+  const unsigned groups = (unsigned)((p.num_rows + p.G - 1) / p.G);
+  const size_t planes = (size_t)p.G * ((size_t)(p.kv_len + 31) / 32) * sizeof(uint32_t);
+  if (p.G <= kMaxMembers && planes <= (size_t)kMergeLdsMax) {
+    hipLaunchKernelGGL(union_bitmap_kernel, dim3(groups), dim3(kBitmapThreads), planes, stream, p);
+    return hipGetLastError();
+  }
   switch (p.topk_pad) {
     case 256: launch_sort<4>(p, stream); break;
     case 512: launch_sort<8>(p, stream); break;
@@ -235,7 +355,6 @@ hipError_t launch_union_build(const UnionBuildParams& p, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned groups = (unsigned)((p.num_rows + p.G - 1) / p.G);
   const size_t lists = (size_t)p.G * p.topk_pad * sizeof(int32_t);
   if (lists <= (size_t)kMergeLdsMax)
     hipLaunchKernelGGL(union_merge_kernel<true>, dim3(groups), dim3(kMergeThreads), lists, stream, p);
