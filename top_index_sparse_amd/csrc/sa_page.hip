@@ -31,13 +31,16 @@ __global__ void __launch_bounds__(kThreads) page_mark_kernel(const int32_t* idx,
   if (t >= 0 && (int64_t)t < pool_tokens) mask[t / src_page_tokens] = 1;
 }
 
-// Copies n bytes; eight 16-byte loads per thread are issued before their
-// stores so that a page costs about two memory round trips, not eleven.
+// Copies n bytes; sixteen 16-byte loads per thread are issued before their
+// stores, so a 64-row destination page (10.25 chunks per thread) costs one
+// memory round trip.
+// Both sides are streamed (non-temporal): the pool pages are read once and
+// the destination is not read back by this kernel.
 template <bool VEC16>
 __device__ __forceinline__ void copy_bytes(uint8_t* __restrict__ dst, const uint8_t* __restrict__ src,
                                            int64_t n) {
   if (VEC16) {
-    constexpr int U = 8;
+    constexpr int U = 16;
     const int64_t nv = n >> 4;
     const u32x4_t* s = reinterpret_cast<const u32x4_t*>(src);
     u32x4_t* d = reinterpret_cast<u32x4_t*>(dst);
@@ -45,10 +48,10 @@ __device__ __forceinline__ void copy_bytes(uint8_t* __restrict__ dst, const uint
       u32x4_t v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (i + u * kThreads < nv) v[u] = s[i + u * kThreads];
+        if (i + u * kThreads < nv) v[u] = __builtin_nontemporal_load(&s[i + u * kThreads]);
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (i + u * kThreads < nv) d[i + u * kThreads] = v[u];
+        if (i + u * kThreads < nv) __builtin_nontemporal_store(v[u], &d[i + u * kThreads]);
     }
   } else {
     for (int64_t i = threadIdx.x; i < n; i += kThreads) dst[i] = src[i];
