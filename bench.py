@@ -243,7 +243,18 @@ def measure_others(args, sa, torch, stream):
         q, k, v, idx, cu_q, cu_kv, sm_scale=c.scale, out=out, lse=lse, stream=stream), w, n)
     res["ragged_chunk_prefill"] = _rate(gathered_bytes(c), ms)
     res["ragged_chunk_prefill"]["rows"] = c.num_rows
-    del q, k, v, idx, out, lse
+    # union mode over the same ragged requests (groups of 2 rows per request)
+    ws = torch.empty(sa.sparse_attn_chunk_union_workspace_bytes(c.num_rows, len(cu_q) - 1,
+                                                                c.topk, 2),
+                     dtype=torch.uint8, device="cuda")
+    ms_u = _events_ms(torch, stream, lambda: sa.sparse_attn_chunk_prefill_union(
+        q, k, v, idx, cu_q, cu_kv, 2, sm_scale=c.scale, ws=ws, out=out, lse=lse,
+        stream=stream), w, n)
+    r = _rate(gathered_bytes(c), ms_u)
+    r = {"ms": r["ms"], "per_token_equivalent_GBps": r["GBps"],
+         "speedup_vs_per_token": round(ms / ms_u, 3)}
+    res["ragged_chunk_prefill_union_G2"] = r
+    del q, k, v, idx, out, lse, ws
 
     # decode page mark + masked split vs full split
     c = gen.make_config("C4decode", args.seed)

@@ -177,6 +177,38 @@ sa_status sparse_attn_prefill_union(const sa_attn_desc* desc, const void* q, con
                                     int32_t kv_len, int32_t G, void* ws, size_t ws_bytes,
                                     float* out, float* lse, hipStream_t stream);
 
+/* Bytes of device workspace sparse_attn_chunk_prefill_union needs (0 on
+ * invalid sizes). Layout, each part 256-byte aligned, with
+ * groups = ceil(total_q / G) + num_reqs and stride = align16(G * topk):
+ * int32 first group id per request [num_reqs + 1], then int32 union_idx
+ * [groups][stride], uint8 union_bits [groups][stride], int32 union_len
+ * [groups] (the union_build layout per group, request-local indices; groups
+ * listed request by request). */
+size_t sparse_attn_chunk_union_workspace_bytes(int32_t total_q, int32_t num_reqs, int32_t topk,
+                                               int32_t G);
+
+/* Union-mode ragged chunk prefill: the union of sparse_attn_prefill_union
+ * (sglang PR 32779, "Modifications") over the requests of
+ * sparse_attn_chunk_prefill (PR 37275, "Kernel measurements": the chunk
+ * kernel). Groups are G consecutive rows inside one request (the last group
+ * of a request may be short) and never span requests; indices are local to
+ * their request's KV range, as in sparse_attn_chunk_prefill. Every row's
+ * result is the per-token result over its distinct valid indices.
+ * Legal iff G * group <= 32; otherwise the per-token ragged path runs and
+ * SA_OK_FALLBACK is returned.
+ * cu_seqlens_q   device int32 [num_reqs + 1], non-decreasing, last = total_q
+ * cu_seqlens_kv  device int64 [num_reqs + 1], KV rows below 2^31 in total
+ * ws             device workspace of sparse_attn_chunk_union_workspace_bytes,
+ *                256-byte aligned, used only during the call
+ * Nothing is read back to the host; the grid depends on host scalars only.
+ */
+sa_status sparse_attn_chunk_prefill_union(const sa_attn_desc* desc, const void* q, const void* k,
+                                          const void* v, const int32_t* idx,
+                                          const int32_t* cu_seqlens_q,
+                                          const int64_t* cu_seqlens_kv, int32_t num_reqs,
+                                          int32_t total_q, int32_t G, void* ws, size_t ws_bytes,
+                                          float* out, float* lse, hipStream_t stream);
+
 /* Decode-pool page geometry (sglang PR 32320, "Modifications"). A source
  * page holds src_page_tokens rows of row_bytes followed by src_page_tokens
  * scales of scale_bytes; a destination page holds dst_page_tokens rows then
@@ -230,7 +262,8 @@ typedef enum {
   SA_ENTRY_PREFILL_UNION = 3,
   SA_ENTRY_PAGE_MARK = 4,
   SA_ENTRY_PAGE_SPLIT = 5,
-  SA_ENTRY_COUNT = 6
+  SA_ENTRY_CHUNK_PREFILL_UNION = 6,
+  SA_ENTRY_COUNT = 7
 } sa_entry;
 uint64_t sa_call_count(int32_t entry);
 

@@ -22,7 +22,7 @@ brute force, closed forms, Python-set semantics, numpy reshapes); none is
 "parity unpinned".
 """
 from .attention import bf16_to_f64, sparse_attention, chunk_prefill, row_attention
-from .union import union_build, union_attention
+from .union import union_build, union_attention, chunk_union_build, chunk_union_attention
 from .pages import page_mark, page_split
 
 __all__ = [
@@ -32,6 +32,8 @@ __all__ = [
     "row_attention",
     "union_build",
     "union_attention",
+    "chunk_union_build",
+    "chunk_union_attention",
     "page_mark",
     "page_split",
 ]

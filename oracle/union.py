@@ -88,3 +88,62 @@ def union_attention(q: np.ndarray, k: np.ndarray, v, union_idx: np.ndarray,
             out[r, heads] = o
             lse[r, heads] = s
     return out, lse
+
+
+def chunk_union_build(idx: np.ndarray, cu_seqlens_q: np.ndarray, cu_seqlens_kv: np.ndarray,
+                      G: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Union sets over ragged requests: the union of PR 32779 ("Modifications")
+    applied to the requests of the chunk kernel (PR 37275, "Kernel
+    measurements"). Request r owns rows [cu_q[r], cu_q[r+1]) and KV rows
+    [cu_kv[r], cu_kv[r+1]); its groups are G consecutive rows of its own
+    (the last one may be short), so no group spans two requests, and its
+    indices are local to its KV range. Groups are listed request by request.
+
+    Returns union_idx int32 [groups, G*k], union_bits uint8 [same],
+    union_len int32 [groups] (request-local indices, the union_build layout
+    within each group) and group_request int32 [groups]."""
+    T, k = idx.shape
+    parts_i, parts_b, parts_l, owner = [], [], [], []
+    for r in range(len(cu_seqlens_q) - 1):
+        q0, q1 = int(cu_seqlens_q[r]), int(cu_seqlens_q[r + 1])
+        if q1 <= q0:
+            continue
+        kv_len = int(cu_seqlens_kv[r + 1] - cu_seqlens_kv[r])
+        ui, ub, ul = union_build(idx[q0:q1], kv_len, G)
+        parts_i.append(ui)
+        parts_b.append(ub)
+        parts_l.append(ul)
+        owner.append(np.full(len(ul), r, dtype=np.int32))
+    if not parts_l:
+        return (np.zeros((0, G * k), np.int32), np.zeros((0, G * k), np.uint8),
+                np.zeros(0, np.int32), np.zeros(0, np.int32))
+    return (np.concatenate(parts_i), np.concatenate(parts_b), np.concatenate(parts_l),
+            np.concatenate(owner))
+
+
+def chunk_union_attention(q: np.ndarray, k: np.ndarray, v, union_idx: np.ndarray,
+                          union_bits: np.ndarray, union_len: np.ndarray,
+                          group_request: np.ndarray, cu_seqlens_q: np.ndarray,
+                          cu_seqlens_kv: np.ndarray, G: int, *, num_kv_heads: int,
+                          scale: float, head_dim_v=None,
+                          rows=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Union attention of each request's rows over its own groups' lists and
+    its own KV range (the per-row definition of union_attention)."""
+    T = q.shape[0]
+    dv = head_dim_v if v is None else v.shape[2]
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    out = np.zeros((len(rows), q.shape[1], dv))
+    lse = np.zeros((len(rows), q.shape[1]))
+    req = np.searchsorted(cu_seqlens_q, rows, side="right") - 1
+    for r in np.unique(req):
+        sel = np.flatnonzero(req == r)
+        q0, q1 = int(cu_seqlens_q[r]), int(cu_seqlens_q[r + 1])
+        lo, hi = int(cu_seqlens_kv[r]), int(cu_seqlens_kv[r + 1])
+        g = np.flatnonzero(group_request == r)
+        o, s = union_attention(q[q0:q1], k[lo:hi], None if v is None else v[lo:hi],
+                               union_idx[g], union_bits[g], union_len[g], G,
+                               num_kv_heads=num_kv_heads, scale=scale, head_dim_v=head_dim_v,
+                               rows=rows[sel] - q0)
+        out[sel] = o
+        lse[sel] = s
+    return out, lse

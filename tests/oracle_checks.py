@@ -274,6 +274,70 @@ def check_union_equals_per_token(union_attention, sparse_attention, union_build,
         assert np.abs(a[1] - b[1]).max() <= 1e-12, "union LSE"
 
 
+def check_chunk_union_dense(chunk_union_build, chunk_union_attention, seed=11):
+    """Ragged requests whose rows index their visible prefix (permuted, no
+    duplicates, -1 tails) give dense causal attention per request through
+    the ragged union; groups never span requests, so rows of different
+    requests with the same local indices still see their own KV range."""
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, D = 4, 1, 16
+    qlens, ctxs = [5, 0, 3, 7], [9, 4, 3, 12]
+    cu_q = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    cu_kv = np.concatenate([[0], np.cumsum(ctxs)]).astype(np.int64)
+    T, KV, width = int(cu_q[-1]), int(cu_kv[-1]), 14
+    q = gen.normal_bf16(rng, (T, Hq, D))
+    k = gen.normal_bf16(rng, (KV, Hkv, D))
+    v = gen.normal_bf16(rng, (KV, Hkv, D))
+    idx = np.full((T, width), -1, np.int32)
+    ro = np.zeros((T, Hq, D))
+    rl = np.zeros((T, Hq))
+    for r in range(len(qlens)):
+        if qlens[r] == 0:
+            continue
+        mask = np.full((qlens[r], ctxs[r]), -np.inf)
+        for i in range(qlens[r]):
+            p = ctxs[r] - qlens[r] + i
+            idx[cu_q[r] + i, :p + 1] = rng.permutation(p + 1)
+            idx[cu_q[r] + i, p + 1] = ctxs[r] + 2          # out of its request's range
+            mask[i, :p + 1] = 0
+        rows = slice(cu_q[r], cu_q[r + 1])
+        kvs = slice(cu_kv[r], cu_kv[r + 1])
+        o, l = _dense_reference(q[rows], k[kvs], v[kvs], mask, 0.3, Hkv)
+        ro[rows], rl[rows] = o, l
+    for G in (2, 3, 4):
+        ui, ub, ul, gr = chunk_union_build(idx, cu_q, cu_kv, G)
+        want = sum((n + G - 1) // G for n in qlens)
+        assert len(ul) == want, ("group count", G)
+        o, lse = chunk_union_attention(q, k, v, ui, ub, ul, gr, cu_q, cu_kv, G,
+                                       num_kv_heads=Hkv, scale=0.3)
+        assert np.abs(o - ro).max() <= 1e-12, ("chunk union O", G)
+        assert np.abs(lse - rl).max() <= 1e-12, ("chunk union LSE", G)
+
+
+def check_chunk_union_equals_per_token(chunk_union_build, chunk_union_attention, chunk_prefill,
+                                       seed=12):
+    """On duplicate-free walk rows over ragged requests the ragged union
+    equals the per-token chunk prefill."""
+    rng = np.random.default_rng(seed)
+    qlens, ctxs = [6, 3, 1, 9], [20, 12, 8, 30]
+    cu_q = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    cu_kv = np.concatenate([[0], np.cumsum(ctxs)]).astype(np.int64)
+    T, KV, width, Hq, D = int(cu_q[-1]), int(cu_kv[-1]), 7, 6, 8
+    q = gen.normal_bf16(rng, (T, Hq, D))
+    k = gen.normal_bf16(rng, (KV, 1, D))
+    v = gen.normal_bf16(rng, (KV, 1, D))
+    idx = np.concatenate([gen.random_walk_indices(rng, np.arange(c - n, c), width, swap_frac=0.3)
+                          for n, c in zip(qlens, ctxs)]).astype(np.int32)
+    idx[1, 2] = -1
+    b = chunk_prefill(q, k, v, idx, cu_q, cu_kv, num_kv_heads=1, scale=0.4)
+    for G in (2, 4):
+        ui, ub, ul, gr = chunk_union_build(idx, cu_q, cu_kv, G)
+        a = chunk_union_attention(q, k, v, ui, ub, ul, gr, cu_q, cu_kv, G, num_kv_heads=1,
+                                  scale=0.4)
+        assert np.abs(a[0] - b[0]).max() <= 1e-12, ("chunk union vs per-token O", G)
+        assert np.abs(a[1] - b[1]).max() <= 1e-12, ("chunk union vs per-token LSE", G)
+
+
 # --------------------------------------------------------------------------
 # pages
 

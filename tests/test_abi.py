@@ -177,3 +177,37 @@ def test_prefill_union_rejects_on_host():
                                        None, 0, 0x4000, 0x5000, None)
     assert st == -5
     assert "workspace" in sa.sa_last_error()
+
+
+def test_chunk_union_workspace_and_host_rejections():
+    # first group ids, then at most ceil(total_q / G) + num_reqs groups of
+    # align16(G * topk) int32 + uint8 rows and their lengths
+    groups = (28988 + 1) // 2 + 16
+    stride = (2 * 2051 + 15) // 16 * 16
+    n = sa.sparse_attn_chunk_union_workspace_bytes(28988, 16, 2051, 2)
+    assert n >= 17 * 4 + groups * stride * 5 + groups * 4 and n % 256 == 0
+    assert sa.sparse_attn_chunk_union_workspace_bytes(10, 0, 20, 2) == 0
+    assert sa.sparse_attn_chunk_union_workspace_bytes(10, 2, 20, 9) == 0
+    assert sa.sparse_attn_chunk_union_workspace_bytes(-1, 2, 20, 2) == 0
+    lib = sa.lib()
+    d = _desc()
+    f = lib.sparse_attn_chunk_prefill_union
+    # rows but no request; missing cu_seqlens; missing and short workspace;
+    # misaligned workspace; bad G
+    assert f(ctypes.byref(d), None, None, None, None, None, None, 0, 5, 2, None, 0, None, None,
+             None) == -2
+    assert f(ctypes.byref(d), 0x1000, 0x2000, 0x3000, 0x4000, None, None, 2, 5, 2, 0x7000, 1 << 20,
+             0x5000, 0x6000, None) == -1
+    assert f(ctypes.byref(d), 0x1000, 0x2000, 0x3000, 0x4000, 0x8000, 0x9000, 2, 5, 2, None, 0,
+             0x5000, 0x6000, None) == -5
+    assert f(ctypes.byref(d), 0x1000, 0x2000, 0x3000, 0x4000, 0x8000, 0x9000, 2, 5, 2, 0x7000, 64,
+             0x5000, 0x6000, None) == -5
+    assert f(ctypes.byref(d), 0x1000, 0x2000, 0x3000, 0x4000, 0x8000, 0x9000, 2, 5, 2, 0x7010,
+             1 << 20, 0x5000, 0x6000, None) == -2
+    assert f(ctypes.byref(d), 0x1000, 0x2000, 0x3000, 0x4000, 0x8000, 0x9000, 2, 5, 9, 0x7000,
+             1 << 20, 0x5000, 0x6000, None) == -2
+    # no rows: nothing to launch, counted
+    before = sa.sa_call_count("sparse_attn_chunk_prefill_union")
+    assert f(ctypes.byref(d), None, None, None, None, None, None, 0, 0, 2, None, 0, None, None,
+             None) == 0
+    assert sa.sa_call_count("sparse_attn_chunk_prefill_union") == before + 1

@@ -275,3 +275,69 @@ def test_pins_catch_page_mistakes():
 
     for bad in (split_ignores_mask, split_scale_offset):
         assert _fails_some([lambda b=bad: C.check_page_split(b)])
+
+
+# ragged union -------------------------------------------------------------
+
+def _one_request_build(idx, kv_len, G):
+    ui, ub, ul, _ = oracle.chunk_union_build(idx, np.array([0, idx.shape[0]], np.int32),
+                                             np.array([0, kv_len], np.int64), G)
+    return ui, ub, ul
+
+
+def test_chunk_union_single_request_is_the_union_build():
+    # one request reduces to the pinned single-batch contract and fixture
+    C.check_union_golden(_one_request_build)
+    C.check_union_contract(_one_request_build)
+
+
+def test_chunk_union_dense():
+    C.check_chunk_union_dense(oracle.chunk_union_build, oracle.chunk_union_attention)
+
+
+def test_chunk_union_equals_per_token():
+    C.check_chunk_union_equals_per_token(oracle.chunk_union_build, oracle.chunk_union_attention,
+                                         oracle.chunk_prefill)
+
+
+def test_pins_catch_chunk_union_mistakes():
+    # groups formed over the whole batch, spanning requests
+    def spanning(idx, cu_q, cu_kv, G):
+        ui, ub, ul = oracle.union_build(idx, int(cu_kv[-1]), G)
+        starts = np.arange(0, idx.shape[0], G)
+        return ui, ub, ul, (np.searchsorted(cu_q, starts, side="right") - 1).astype(np.int32)
+    assert _fails_some([lambda: C.check_chunk_union_dense(spanning, oracle.chunk_union_attention)])
+    # attention reading from the start of the KV buffer, not the request's range
+    assert _fails_some([lambda: C.check_chunk_union_dense(oracle.chunk_union_build,
+                                                          _no_base_attention)])
+    # validity checked against the whole KV buffer, not the request's length
+    assert _fails_some([lambda: C.check_chunk_union_dense(_loose_build,
+                                                          oracle.chunk_union_attention)])
+
+
+def _no_base_attention(q, k, v, ui, ub, ul, gr, cu_q, cu_kv, G, *, num_kv_heads, scale,
+                       head_dim_v=None, rows=None):
+    T = q.shape[0]
+    dv = v.shape[2]
+    out = np.zeros((T, q.shape[1], dv))
+    lse = np.zeros((T, q.shape[1]))
+    for r in range(len(cu_q) - 1):
+        q0, q1 = int(cu_q[r]), int(cu_q[r + 1])
+        if q1 <= q0:
+            continue
+        g = np.flatnonzero(gr == r)
+        o, s = oracle.union_attention(q[q0:q1], k, v, ui[g], ub[g], ul[g], G,
+                                      num_kv_heads=num_kv_heads, scale=scale)
+        out[q0:q1], lse[q0:q1] = o, s
+    return out, lse
+
+
+def _loose_build(idx, cu_q, cu_kv, G):
+    parts = []
+    for r in range(len(cu_q) - 1):
+        q0, q1 = int(cu_q[r]), int(cu_q[r + 1])
+        if q1 <= q0:
+            continue
+        ui, ub, ul = oracle.union_build(idx[q0:q1], int(cu_kv[-1]), G)
+        parts.append((ui, ub, ul, np.full(len(ul), r, np.int32)))
+    return tuple(np.concatenate([p[i] for p in parts]) for i in range(4))

@@ -24,6 +24,8 @@ __all__ = [
     "sparse_attn_union_workspace_bytes",
     "sparse_attn_union_build",
     "sparse_attn_prefill_union",
+    "sparse_attn_chunk_union_workspace_bytes",
+    "sparse_attn_chunk_prefill_union",
     "page_mark",
     "page_split",
     "sa_validate_attn",
@@ -46,7 +48,7 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_OK_FALLBACK", -1: "SA_ERR_NULL", -2: "SA_ERR_
                 -6: "SA_ERR_HIP"}
 ENTRIES = {"sparse_attn_prefill": 0, "sparse_attn_chunk_prefill": 1,
            "sparse_attn_union_build": 2, "sparse_attn_prefill_union": 3,
-           "page_mark": 4, "page_split": 5}
+           "page_mark": 4, "page_split": 5, "sparse_attn_chunk_prefill_union": 6}
 
 
 class SparseAttnError(RuntimeError):
@@ -96,6 +98,9 @@ _SIGNATURES = {
                                        _P]),
     "sparse_attn_prefill_union": (_I32, [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _I32, _I32,
                                          _I32, _P, _SZ, _P, _P, _P]),
+    "sparse_attn_chunk_union_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "sparse_attn_chunk_prefill_union": (_I32, [ctypes.POINTER(AttnDesc), _P, _P, _P, _P, _P, _P,
+                                               _I32, _I32, _I32, _P, _SZ, _P, _P, _P]),
     "page_mark": (_I32, [_P, _I64, _I32, _I32, _P, _P]),
     "page_split": (_I32, [ctypes.POINTER(PageDesc), _P, _P, _P, _I32, _P]),
     "sa_validate_attn": (ctypes.c_int, [ctypes.POINTER(AttnDesc), _I32]),
@@ -346,6 +351,41 @@ def sparse_attn_prefill_union(q: torch.Tensor, k: torch.Tensor, v: Optional[torc
                                          ws.numel() * ws.element_size(), _ptr(out), _ptr(lse),
                                          _stream(stream))
     return out, lse, _check(st, "sparse_attn_prefill_union")
+
+
+def sparse_attn_chunk_union_workspace_bytes(total_q: int, num_reqs: int, topk: int,
+                                            G: int) -> int:
+    return int(lib().sparse_attn_chunk_union_workspace_bytes(total_q, num_reqs, topk, G))
+
+
+def sparse_attn_chunk_prefill_union(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor],
+                                    idx: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                                    cu_seqlens_kv: torch.Tensor, G: int, *,
+                                    total_q: Optional[int] = None,
+                                    sm_scale: Optional[float] = None,
+                                    head_dim_v: Optional[int] = None,
+                                    ws: Optional[torch.Tensor] = None,
+                                    out: Optional[torch.Tensor] = None,
+                                    lse: Optional[torch.Tensor] = None, stream=None):
+    """Union-mode ragged chunk prefill (C: sparse_attn_chunk_prefill_union).
+    Groups of G rows never span requests. Returns (out, lse, status) where
+    status is SA_OK or SA_OK_FALLBACK."""
+    T = q.shape[0] if total_q is None else int(total_q)
+    desc, out, lse = _prep_attn(q, k, v, idx, sm_scale, head_dim_v, out, lse, T)
+    _need(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1, q.device)
+    _need(cu_seqlens_kv, "cu_seqlens_kv", torch.int64, 1, q.device)
+    R = cu_seqlens_q.shape[0] - 1
+    if cu_seqlens_kv.shape[0] != R + 1 or not cu_seqlens_q.is_contiguous() \
+            or not cu_seqlens_kv.is_contiguous():
+        raise ValueError("cu_seqlens_q/kv must be contiguous [R+1]")
+    nbytes = sparse_attn_chunk_union_workspace_bytes(T, max(R, 1), idx.shape[1], G)
+    ws = _workspace(ws, nbytes, q.device)
+    st = lib().sparse_attn_chunk_prefill_union(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(idx), _ptr(cu_seqlens_q),
+                                               _ptr(cu_seqlens_kv), R, T, G, _ptr(ws),
+                                               ws.numel() * ws.element_size(), _ptr(out),
+                                               _ptr(lse), _stream(stream))
+    return out, lse, _check(st, "sparse_attn_chunk_prefill_union")
 
 
 def page_mark(idx: torch.Tensor, num_src_pages: int, src_page_tokens: int, *,

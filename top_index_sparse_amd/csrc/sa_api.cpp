@@ -165,6 +165,27 @@ bool union_layout(int32_t num_rows, int32_t topk, int32_t G, UnionLayout* L) {
   return true;
 }
 
+// Workspace layout of chunk_prefill_union: per-request first group ids,
+// then the union lists of at most ceil(total_q / G) + num_reqs groups.
+struct ChunkUnionLayout {
+  int64_t groups, stride;
+  int64_t gstart_off, idx_off, bits_off, len_off, total;
+};
+
+bool chunk_union_layout(int32_t total_q, int32_t num_reqs, int32_t topk, int32_t G,
+                        ChunkUnionLayout* L) {
+  if (total_q < 0 || num_reqs < 1 || topk <= 0 || G < 1 || G > 8) return false;
+  L->groups = ((int64_t)total_q + G - 1) / G + num_reqs;
+  if (L->groups > INT32_MAX) return false;
+  L->stride = align_up((int64_t)G * topk, 16);
+  L->gstart_off = 0;
+  L->idx_off = align_up(((int64_t)num_reqs + 1) * 4, 256);
+  L->bits_off = L->idx_off + align_up(L->groups * L->stride * 4, 256);
+  L->len_off = L->bits_off + align_up(L->groups * L->stride, 256);
+  L->total = L->len_off + align_up(L->groups * 4, 256);
+  return true;
+}
+
 sa::UnionBuildParams build_params(const int32_t* idx, int64_t idx_row_stride, int32_t num_rows,
                                   int32_t topk, int32_t kv_len, int32_t G, const UnionLayout& L,
                                   void* ws) {
@@ -325,6 +346,77 @@ sa_status sparse_attn_prefill_union(const sa_attn_desc* desc, const void* q, con
   p.num_groups = (int32_t)L.groups;
   st = launch_attention(kernel, p, 1, stream);
   return st == SA_OK ? ok(SA_ENTRY_PREFILL_UNION) : st;
+}
+
+size_t sparse_attn_chunk_union_workspace_bytes(int32_t total_q, int32_t num_reqs, int32_t topk,
+                                               int32_t G) {
+  ChunkUnionLayout L;
+  if (!chunk_union_layout(total_q, num_reqs, topk, G, &L)) return 0;
+  return (size_t)L.total;
+}
+
+sa_status sparse_attn_chunk_prefill_union(const sa_attn_desc* desc, const void* q, const void* k,
+                                          const void* v, const int32_t* idx,
+                                          const int32_t* cu_seqlens_q,
+                                          const int64_t* cu_seqlens_kv, int32_t num_reqs,
+                                          int32_t total_q, int32_t G, void* ws, size_t ws_bytes,
+                                          float* out, float* lse, hipStream_t stream) {
+  g_err[0] = 0;
+  Kernel kernel = Kernel::kNone;
+  const sa_status legal = check_desc(desc, G, &kernel);
+  if (legal != SA_OK && legal != SA_OK_FALLBACK) return legal;
+  if (num_reqs < 0 || total_q < 0)
+    return fail(SA_ERR_SHAPE, "num_reqs %d and total_q %d must be >= 0", num_reqs, total_q);
+  if (total_q == 0 || num_reqs == 0) {
+    if (total_q != 0) return fail(SA_ERR_SHAPE, "total_q %d rows but no request", total_q);
+    return ok(SA_ENTRY_CHUNK_PREFILL_UNION, legal);
+  }
+  if (!cu_seqlens_q || !cu_seqlens_kv) return fail(SA_ERR_NULL, "cu_seqlens_q/kv are required");
+  sa_status st = check_ptrs(desc, q, k, v, idx, out, lse);
+  if (st != SA_OK) return st;
+  sa::AttnParams p = make_params(desc, q, k, v, idx, out, lse, total_q);
+  p.cu_q = cu_seqlens_q;
+  p.cu_kv = cu_seqlens_kv;
+  p.num_reqs = num_reqs;
+  if (legal == SA_OK_FALLBACK) {
+    // G * group > 32: the per-token path gives every row its own result
+    st = launch_attention(kernel, p, 0, stream);
+    return st == SA_OK ? ok(SA_ENTRY_CHUNK_PREFILL_UNION, SA_OK_FALLBACK) : st;
+  }
+  ChunkUnionLayout L;
+  if (!chunk_union_layout(total_q, num_reqs, desc->topk, G, &L))
+    return fail(SA_ERR_SHAPE, "too many union groups for one launch");
+  if (!ws || ws_bytes < (size_t)L.total)
+    return fail(SA_ERR_WORKSPACE, "workspace of %zu bytes, %lld needed", ws_bytes,
+                (long long)L.total);
+  if (reinterpret_cast<uintptr_t>(ws) & 255) return fail(SA_ERR_SHAPE, "ws must be 256-byte aligned");
+  char* base = static_cast<char*>(ws);
+  int32_t* gstart = reinterpret_cast<int32_t*>(base + L.gstart_off);
+  sa::UnionBuildParams b{};
+  b.idx = idx;
+  b.idx_row_stride = desc->idx_row_stride;
+  b.num_rows = total_q;
+  b.topk = desc->topk;
+  b.G = G;
+  b.union_idx = reinterpret_cast<int32_t*>(base + L.idx_off);
+  b.union_bits = reinterpret_cast<uint8_t*>(base + L.bits_off);
+  b.union_len = reinterpret_cast<int32_t*>(base + L.len_off);
+  b.union_stride = L.stride;
+  b.cu_q = cu_seqlens_q;
+  b.cu_kv = cu_seqlens_kv;
+  b.num_reqs = num_reqs;
+  b.num_groups = (int32_t)L.groups;
+  hipError_t e = sa::launch_union_build_ragged(b, gstart, stream);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  p.union_idx = b.union_idx;
+  p.union_bits = b.union_bits;
+  p.union_len = b.union_len;
+  p.union_stride = L.stride;
+  p.G = G;
+  p.num_groups = (int32_t)L.groups;
+  p.gstart = gstart;
+  st = launch_attention(kernel, p, 1, stream);
+  return st == SA_OK ? ok(SA_ENTRY_CHUNK_PREFILL_UNION) : st;
 }
 
 sa_status page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src_pages,

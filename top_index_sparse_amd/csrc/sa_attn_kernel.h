@@ -147,6 +147,7 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   int jmax;                   // slots the team streams
   int base_l = 0;             // per-token: first KV row of this lane's request
   int len_l = 0;              // and its length
+  int64_t team_kv = 0;        // union over ragged requests: the group's first KV row
   if (UNION) {
     const int per_head = p.num_groups * p.teams_per_group;
     kvh = team_id / per_head;
@@ -154,17 +155,25 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     const int r = team_id - kvh * per_head;
     const int gi = r / p.teams_per_group;
     const int ts = r - gi * p.teams_per_group;
+    int first, members;
+    len_l = p.kv_len;
+    if (p.gstart) {
+      if (!ragged_group(p.gstart, p.cu_q, p.cu_kv, p.num_reqs, p.G, gi, first, members, team_kv,
+                        len_l))
+        return;
+    } else {
+      first = gi * p.G;
+      members = p.G;
+    }
+    if (members > p.num_rows - first) members = p.num_rows - first;   // rows that exist
     bit0 = ts * p.rows_per_team;                      // first member served
-    rows = p.G - bit0;
+    rows = members - bit0;
     if (rows > p.rows_per_team) rows = p.rows_per_team;
-    const int tail = p.num_rows - gi * p.G - bit0;    // rows that exist
-    if (rows > tail) rows = tail;
     if (rows <= 0) return;
-    t0 = gi * p.G + bit0;
+    t0 = first + bit0;
     irow = p.union_idx + (int64_t)gi * p.union_stride;
     brow = p.union_bits + (int64_t)gi * p.union_stride;
     jmax = p.union_len[gi];
-    len_l = p.kv_len;
   } else {
     const int per_head = (p.num_rows + p.rows_per_team - 1) / p.rows_per_team;
     kvh = team_id / per_head;
@@ -214,8 +223,8 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   };
   uint32_t col_bit[C];
   // Wave-uniform K/V bases; lane offsets are added per load.
-  const uint16_t* kw = p.k + kvh * DQK + (VKLDS ? 0 : 32 * KSTEPS * split);
-  const uint16_t* vw = p.v + kvh * (V_IN_K ? DQK : DV) + 128 * VCH * split;
+  const uint16_t* kw = p.k + team_kv * p.k_row_stride + kvh * DQK + (VKLDS ? 0 : 32 * KSTEPS * split);
+  const uint16_t* vw = p.v + team_kv * p.v_row_stride + kvh * (V_IN_K ? DQK : DV) + 128 * VCH * split;
 
   // ---- Q^T operands: lane (g, n) of tile c holds column n, d = 32s + 8g ----
   u32x4_t qop[C][KSTEPS];

@@ -37,6 +37,7 @@ struct AttnParams {
   int64_t union_stride;
   int32_t G;
   int32_t num_groups;
+  const int32_t* gstart;      // union over ragged requests: first group id per request
   int32_t teams_per_group;    // union: teams serving one group
   // rows one team serves (per-token: consecutive rows; union: group members)
   int32_t rows_per_team;
@@ -55,7 +56,36 @@ struct UnionBuildParams {
   uint8_t* union_bits;        // [groups][union_stride]
   int32_t* union_len;         // [groups]
   int64_t union_stride;
+  // ragged groups (chunk prefill): G rows inside each request, request-local
+  // indices; group ids [gstart[r], gstart[r+1]) belong to request r
+  const int32_t* gstart;      // nullable: one request of kv_len
+  const int32_t* cu_q;
+  const int64_t* cu_kv;
+  int32_t num_reqs;
+  int32_t num_groups;         // groups launched (an upper bound when ragged)
+  int32_t plane_words;        // 32-token words per member per bit-plane chunk
 };
+
+// Ragged union groups: ids [gstart[r], gstart[r+1]) belong to request r,
+// each covering G consecutive rows of it (the last may be short). False for
+// ids past the last group.
+__device__ __forceinline__ bool ragged_group(const int32_t* gstart, const int32_t* cu_q,
+                                             const int64_t* cu_kv, int num_reqs, int G, int gi,
+                                             int& first, int& members, int64_t& kv_base,
+                                             int& kv_len) {
+  if (gi >= gstart[num_reqs]) return false;
+  int lo = 0, hi = num_reqs - 1;   // last request whose first group id is <= gi
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (gstart[mid] <= gi) lo = mid; else hi = mid - 1;
+  }
+  first = cu_q[lo] + (gi - gstart[lo]) * G;
+  const int end = cu_q[lo + 1];
+  members = end - first < G ? end - first : G;
+  kv_base = cu_kv[lo];
+  kv_len = (int)(cu_kv[lo + 1] - cu_kv[lo]);
+  return true;
+}
 
 struct PageParams {
   const uint8_t* src;
@@ -75,6 +105,9 @@ struct PageParams {
 hipError_t launch_attn_gqa256(AttnParams p, int union_mode, hipStream_t stream);
 hipError_t launch_attn_mla576(AttnParams p, int union_mode, hipStream_t stream);
 hipError_t launch_union_build(const UnionBuildParams& p, hipStream_t stream);
+// Ragged: writes gstart[0..num_reqs] from cu_q, then builds every group's
+// union over its request's KV range with bit planes.
+hipError_t launch_union_build_ragged(UnionBuildParams p, int32_t* gstart, hipStream_t stream);
 hipError_t launch_page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src_pages,
                             int32_t src_page_tokens, int8_t* mask, hipStream_t stream);
 hipError_t launch_page_split(const PageParams& p, hipStream_t stream);

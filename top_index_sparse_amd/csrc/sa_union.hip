@@ -228,49 +228,14 @@ __global__ void __launch_bounds__(kMergeThreads) union_merge_kernel(UnionBuildPa
 
 constexpr int kBitmapThreads = 256;
 constexpr int kMaxMembers = 8;
+constexpr int kRaggedPlaneBytes = 16384;
 
-__global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuildParams p) {
-  extern __shared__ uint32_t planes[];   // [members][W]
-  __shared__ int32_t wave_tot[kBitmapThreads / 64][kMaxMembers];
-  const int gi = blockIdx.x;
-  const int first = gi * p.G;
-  int members = p.num_rows - first;
-  if (members > p.G) members = p.G;
-  const int W = (p.kv_len + 31) >> 5;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  for (int i = tid; i < members * W; i += kBitmapThreads) planes[i] = 0u;
-  __syncthreads();
-  for (int j = 0; j < members; ++j) {
-    const int32_t* row = p.idx + (int64_t)(first + j) * p.idx_row_stride;
-    uint32_t* plane = planes + j * W;
-    for (int e = tid; e < p.topk; e += kBitmapThreads) {
-      const int32_t x = row[e];
-      if ((unsigned)x < (unsigned)p.kv_len) atomicOr(&plane[x >> 5], 1u << (x & 31));
-    }
-  }
-  __syncthreads();
-
-  // Each thread owns a contiguous range of words; count its tokens per bucket.
-  const int wpt = (W + kBitmapThreads - 1) / kBitmapThreads;
-  const int w0 = min(W, tid * wpt), w1 = min(W, w0 + wpt);
-  int cnt[kMaxMembers];
-#pragma unroll
-  for (int j = 0; j < kMaxMembers; ++j) cnt[j] = 0;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t seen = 0u;
-#pragma unroll
-    for (int j = 0; j < kMaxMembers; ++j) {
-      if (j < members) {
-        const uint32_t b = planes[j * W + w];
-        cnt[j] += __popc(b & ~seen);
-        seen |= b;
-      }
-    }
-  }
-  // Exclusive scan of the counts over threads (thread order = word order),
-  // per bucket; bucket j starts after all tokens of buckets < j.
-  int excl[kMaxMembers];
+// Block-wide exclusive scan of per-thread counts (thread order), for every
+// bucket at once; returns each bucket's total in tot.
+__device__ __forceinline__ void scan_buckets(const int cnt[kMaxMembers], int excl[kMaxMembers],
+                                             int tot[kMaxMembers],
+                                             int32_t (*wave_tot)[kMaxMembers]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < kMaxMembers; ++j) {
     int incl = cnt[j];
@@ -283,8 +248,6 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuild
     if (lane == 63) wave_tot[wave][j] = incl;
   }
   __syncthreads();
-  int pos[kMaxMembers];
-  int base = 0;
 #pragma unroll
   for (int j = 0; j < kMaxMembers; ++j) {
     int before = 0, total = 0;
@@ -294,33 +257,146 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuild
       if (w < wave) before += t;
       total += t;
     }
-    pos[j] = base + before + excl[j];
-    base += total;
+    excl[j] += before;
+    tot[j] = total;
   }
-  const int len = base;
+  __syncthreads();   // wave_tot is reused by the next scan
+}
+
+// One workgroup per group. The token range [0, kv_len) is covered in chunks
+// of 32 * plane_words tokens (one chunk whenever the planes fit); with more
+// than one chunk a first pass counts every bucket so that the second can
+// place each chunk's tokens after the earlier chunks'.
+template <bool RAGGED>
+__global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuildParams p) {
+  extern __shared__ uint32_t planes[];   // [members][plane_words]
+  __shared__ int32_t wave_tot[kBitmapThreads / 64][kMaxMembers];
+  const int gi = blockIdx.x;
+  const int tid = threadIdx.x;
+  int first, members, kv_len;
+  if (RAGGED) {
+    int64_t kv_base;
+    if (!ragged_group(p.gstart, p.cu_q, p.cu_kv, p.num_reqs, p.G, gi, first, members, kv_base,
+                      kv_len))
+      return;
+  } else {
+    first = gi * p.G;
+    members = p.G;
+    kv_len = p.kv_len;
+  }
+  if (members > p.num_rows - first) members = p.num_rows - first;   // rows that exist
+  if (members < 0) members = 0;
 
   int32_t* uidx = p.union_idx + (int64_t)gi * p.union_stride;
   uint8_t* ubits = p.union_bits + (int64_t)gi * p.union_stride;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t b[kMaxMembers];
-#pragma unroll
-    for (int j = 0; j < kMaxMembers; ++j) b[j] = j < members ? planes[j * W + w] : 0u;
-    uint32_t seen = 0u;
-#pragma unroll
-    for (int j = 0; j < kMaxMembers; ++j) {
-      uint32_t fresh = b[j] & ~seen;
-      seen |= b[j];
-      while (fresh) {
-        const int bit = __builtin_ctz(fresh);
-        fresh &= fresh - 1u;
-        uint32_t own = 0u;
-#pragma unroll
-        for (int jj = 0; jj < kMaxMembers; ++jj) own |= ((b[jj] >> bit) & 1u) << jj;
-        uidx[pos[j]] = w * 32 + bit;
-        ubits[pos[j]] = (uint8_t)own;
-        ++pos[j];
+  const int cap = 32 * p.plane_words;
+  const int nchunks = kv_len > 0 ? (kv_len + cap - 1) / cap : 0;
+
+  // Clears the planes, then marks every member's indices in [c0, c0 + 32 W).
+  auto mark = [&](int c0, int W) {
+    for (int i = tid; i < members * W; i += kBitmapThreads) planes[i] = 0u;
+    __syncthreads();
+    for (int j = 0; j < members; ++j) {
+      const int32_t* row = p.idx + (int64_t)(first + j) * p.idx_row_stride;
+      uint32_t* plane = planes + j * W;
+      for (int e = tid; e < p.topk; e += kBitmapThreads) {
+        const int32_t x = row[e];
+        const uint32_t o = (uint32_t)(x - c0);
+        if ((unsigned)x < (unsigned)kv_len && o < (uint32_t)(32 * W)) atomicOr(&plane[o >> 5], 1u << (o & 31));
       }
     }
+    __syncthreads();
+  };
+  // Each thread owns a contiguous range of words; counts its tokens per
+  // bucket (the bucket of a token is its lowest owning member).
+  auto count = [&](int W, int w0, int w1, int cnt[kMaxMembers]) {
+#pragma unroll
+    for (int j = 0; j < kMaxMembers; ++j) cnt[j] = 0;
+    for (int w = w0; w < w1; ++w) {
+      uint32_t seen = 0u;
+#pragma unroll
+      for (int j = 0; j < kMaxMembers; ++j) {
+        if (j < members) {
+          const uint32_t b = planes[j * W + w];
+          cnt[j] += __popc(b & ~seen);
+          seen |= b;
+        }
+      }
+    }
+  };
+  auto words = [&](int c) { const int left = (kv_len - c * cap + 31) >> 5; return left < p.plane_words ? left : p.plane_words; };
+  auto range = [&](int W, int& w0, int& w1) {
+    const int wpt = (W + kBitmapThreads - 1) / kBitmapThreads;
+    w0 = min(W, tid * wpt);
+    w1 = min(W, w0 + wpt);
+  };
+
+  int total[kMaxMembers];
+#pragma unroll
+  for (int j = 0; j < kMaxMembers; ++j) total[j] = 0;
+  if (nchunks > 1) {
+    for (int c = 0; c < nchunks; ++c) {
+      const int W = words(c);
+      int w0, w1, cnt[kMaxMembers], excl[kMaxMembers], tot[kMaxMembers];
+      range(W, w0, w1);
+      mark(c * cap, W);
+      count(W, w0, w1, cnt);
+      scan_buckets(cnt, excl, tot, wave_tot);
+#pragma unroll
+      for (int j = 0; j < kMaxMembers; ++j) total[j] += tot[j];
+    }
+  }
+  int base[kMaxMembers], carry[kMaxMembers];
+  int len = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxMembers; ++j) carry[j] = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    const int W = words(c);
+    const int c0 = c * cap;
+    int w0, w1, cnt[kMaxMembers], excl[kMaxMembers], tot[kMaxMembers];
+    range(W, w0, w1);
+    mark(c0, W);
+    count(W, w0, w1, cnt);
+    scan_buckets(cnt, excl, tot, wave_tot);
+    if (nchunks == 1) {
+#pragma unroll
+      for (int j = 0; j < kMaxMembers; ++j) total[j] = tot[j];
+    }
+    // bucket j starts after every token of buckets < j
+    int acc = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxMembers; ++j) {
+      base[j] = acc;
+      acc += total[j];
+    }
+    len = acc;
+    int pos[kMaxMembers];
+#pragma unroll
+    for (int j = 0; j < kMaxMembers; ++j) pos[j] = base[j] + carry[j] + excl[j];
+    for (int w = w0; w < w1; ++w) {
+      uint32_t b[kMaxMembers];
+#pragma unroll
+      for (int j = 0; j < kMaxMembers; ++j) b[j] = j < members ? planes[j * W + w] : 0u;
+      uint32_t seen = 0u;
+#pragma unroll
+      for (int j = 0; j < kMaxMembers; ++j) {
+        uint32_t fresh = b[j] & ~seen;
+        seen |= b[j];
+        while (fresh) {
+          const int bit = __builtin_ctz(fresh);
+          fresh &= fresh - 1u;
+          uint32_t own = 0u;
+#pragma unroll
+          for (int jj = 0; jj < kMaxMembers; ++jj) own |= ((b[jj] >> bit) & 1u) << jj;
+          uidx[pos[j]] = c0 + w * 32 + bit;
+          ubits[pos[j]] = (uint8_t)own;
+          ++pos[j];
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxMembers; ++j) carry[j] += tot[j];
+    __syncthreads();   // the planes are cleared for the next chunk
   }
   const int64_t width = (int64_t)p.G * p.topk;
   for (int64_t r = len + tid; r < width; r += kBitmapThreads) {
@@ -328,6 +404,43 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuild
     ubits[r] = 0;
   }
   if (tid == 0) p.union_len[gi] = len;
+}
+
+// gstart[r] = sum over r' < r of ceil(q_r' / G), for r = 0 .. num_reqs
+// (one workgroup).
+__global__ void __launch_bounds__(kBitmapThreads) union_group_starts_kernel(const int32_t* cu_q,
+                                                                            int32_t num_reqs,
+                                                                            int32_t G,
+                                                                            int32_t* gstart) {
+  __shared__ int32_t wave_tot[kBitmapThreads / 64];
+  __shared__ int32_t carry_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base <= num_reqs; base += kBitmapThreads) {
+    const int r = base + tid;
+    int q = r < num_reqs ? cu_q[r + 1] - cu_q[r] : 0;
+    if (q < 0) q = 0;
+    const int cnt = (q + G - 1) / G;
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kBitmapThreads / 64; ++w) {
+      if (w < wave) before += wave_tot[w];
+      total += wave_tot[w];
+    }
+    if (r <= num_reqs) gstart[r] = carry_s + before + incl - cnt;
+    __syncthreads();
+    if (tid == 0) carry_s += total;
+    __syncthreads();
+  }
 }
 
 template <int R>
@@ -339,9 +452,12 @@ void launch_sort(const UnionBuildParams& p, hipStream_t stream) {
 
 hipError_t launch_union_build(const UnionBuildParams& p, hipStream_t stream) {
   const unsigned groups = (unsigned)((p.num_rows + p.G - 1) / p.G);
-  const size_t planes = (size_t)p.G * ((size_t)(p.kv_len + 31) / 32) * sizeof(uint32_t);
-  if (p.G <= kMaxMembers && planes <= (size_t)kMergeLdsMax) {
-    hipLaunchKernelGGL(union_bitmap_kernel, dim3(groups), dim3(kBitmapThreads), planes, stream, p);
+  const size_t words = ((size_t)p.kv_len + 31) / 32;
+  if (p.G <= kMaxMembers && (size_t)p.G * words * sizeof(uint32_t) <= (size_t)kMergeLdsMax) {
+    UnionBuildParams q = p;
+    q.plane_words = (int32_t)(words > 0 ? words : 1);   // one chunk
+    hipLaunchKernelGGL(union_bitmap_kernel<false>, dim3(groups), dim3(kBitmapThreads),
+                       (size_t)p.G * q.plane_words * sizeof(uint32_t), stream, q);
     return hipGetLastError();
   }
   switch (p.topk_pad) {
@@ -360,6 +476,20 @@ hipError_t launch_union_build(const UnionBuildParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(union_merge_kernel<true>, dim3(groups), dim3(kMergeThreads), lists, stream, p);
   else
     hipLaunchKernelGGL(union_merge_kernel<false>, dim3(groups), dim3(kMergeThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_union_build_ragged(UnionBuildParams p, int32_t* gstart, hipStream_t stream) {
+  hipLaunchKernelGGL(union_group_starts_kernel, dim3(1), dim3(kBitmapThreads), 0, stream, p.cu_q,
+                     p.num_reqs, p.G, gstart);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  p.gstart = gstart;
+  // 16 KB of planes (65536 tokens per chunk at G = 2): small enough for
+  // several workgroups per CU; longer contexts take more chunks
+  p.plane_words = (int32_t)(kRaggedPlaneBytes / (int)sizeof(uint32_t) / p.G);
+  hipLaunchKernelGGL(union_bitmap_kernel<true>, dim3((unsigned)p.num_groups), dim3(kBitmapThreads),
+                     (size_t)p.G * p.plane_words * sizeof(uint32_t), stream, p);
   return hipGetLastError();
 }
 
