@@ -152,7 +152,8 @@ class AttnCase:
     """One sparse attention workload (host arrays, natural layouts).
 
     q      uint16 bf16 bits [T, Hq, Dqk]
-    k      uint16 bf16 bits [kv_total, Hkv, Dqk]
+    k      uint16 bf16 bits [kv_total, Hkv, Dqk], or uint8 FP8 MLA records
+           [kv_total, Hkv, 656] (mla_fp8_rows)
     v      uint16 bf16 bits [kv_total, Hkv, Dv], or None when V is the first
            Dv columns of each K row (MLA latent rows)
     idx    int32 [T, topk], token indices local to the row's request, -1 pad
@@ -213,17 +214,43 @@ def shuffle_slots(idx: np.ndarray, seed: int) -> np.ndarray:
     return np.random.default_rng(seed).permuted(idx, axis=1)
 
 
+FP8_ROW_BYTES = 656
+
+
+def mla_fp8_rows(rng: np.random.Generator, tokens: int) -> np.ndarray:
+    """FP8 MLA latent records, uint8 [tokens, 656]: 512 E4M3 latent codes,
+    four fp32 block scales, 64 bf16 rope values (the record layout the
+    oracle decodes). The latent values are N(0,1) draws; each 128-value
+    block gets scale amax / 448 (E4M3's largest finite value) and its codes
+    come from torch's float8_e4m3fn cast, so the record looks like a
+    quantised cache row."""
+    import torch
+    x = rng.standard_normal((tokens, 4, 128), dtype=np.float32)
+    scale = (np.abs(x).max(axis=2) / np.float32(448.0)).astype(np.float32)
+    scale[scale == 0] = np.float32(1.0)
+    codes = torch.from_numpy(x / scale[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    rope = normal_bf16(rng, (tokens, 64))
+    out = np.empty((tokens, FP8_ROW_BYTES), dtype=np.uint8)
+    out[:, :512] = codes.numpy().reshape(tokens, 512)
+    out[:, 512:528] = scale.astype("<f4").view(np.uint8)
+    out[:, 528:] = rope.astype("<u2").view(np.uint8)
+    return out
+
+
 def make_attn_case(name: str, *, seed: int, num_rows: int, kv_len: int,
                    first_pos: int, num_q_heads: int, num_kv_heads: int,
                    head_dim_qk: int, head_dim_v: int, topk: int,
                    v_in_k: bool = False, walk: bool = True,
-                   scale: Optional[float] = None) -> AttnCase:
+                   scale: Optional[float] = None, kv_fp8: bool = False) -> AttnCase:
     """One request: query rows at positions first_pos .. first_pos+num_rows-1
-    over a KV buffer of kv_len tokens."""
+    over a KV buffer of kv_len tokens (kv_fp8: FP8 MLA records as K)."""
     rq, rk, rv, ri, _, _ = _streams(seed)
     positions = np.arange(first_pos, first_pos + num_rows, dtype=np.int64)
     q = normal_bf16(rq, (num_rows, num_q_heads, head_dim_qk))
-    k = normal_bf16(rk, (kv_len, num_kv_heads, head_dim_qk))
+    if kv_fp8:
+        k = mla_fp8_rows(rk, kv_len * num_kv_heads).reshape(kv_len, num_kv_heads, FP8_ROW_BYTES)
+    else:
+        k = normal_bf16(rk, (kv_len, num_kv_heads, head_dim_qk))
     v = None if v_in_k else normal_bf16(rv, (kv_len, num_kv_heads, head_dim_v))
     if walk:
         idx = random_walk_indices(ri, positions, topk)
@@ -332,7 +359,8 @@ def make_page_case(name: str, *, seed: int, num_src_pages: int = 4096,
     return PageCase(name, src, idx, src_page_tokens, dst_page_tokens, row_bytes, scale_bytes)
 
 
-CONFIG_NAMES = ("C0a", "C0b", "C1", "C2", "C3", "C3tail", "C4", "C4decode", "C4spread")
+CONFIG_NAMES = ("C0a", "C0b", "C1", "C2", "C3", "C3tail", "C3fp8", "C4", "C4decode",
+                "C4spread")
 
 
 def make_config(name: str, seed: int = 0):
@@ -350,6 +378,7 @@ def make_config(name: str, seed: int = 0):
          row per token (V = first 512 columns), top-k 2048 walk
     C3tail  1023 MLA rows at positions 3073..4095 (a group-size tail for
          union mode)
+    C3fp8  C3 with the latent rows held as 656-byte FP8 records
     C4   16 ragged requests, qlen and context log-uniform in [512, 4096] and
          [8192, 65536], group 6 / one KV head, d 256, top-k 2051 walk
     C4decode  4096-page pool of 256-token pages (656 B rows plus 4 B scales),
@@ -380,6 +409,10 @@ def make_config(name: str, seed: int = 0):
         return make_attn_case(name, seed=seed, num_rows=1023, kv_len=4096,
                               first_pos=4096 - 1023, num_q_heads=8, num_kv_heads=1,
                               head_dim_qk=576, head_dim_v=512, topk=2048, v_in_k=True)
+    if name == "C3fp8":
+        return make_attn_case(name, seed=seed, num_rows=4096, kv_len=4096, first_pos=0,
+                              num_q_heads=8, num_kv_heads=1, head_dim_qk=576,
+                              head_dim_v=512, topk=2048, v_in_k=True, kv_fp8=True)
     if name == "C4":
         return make_ragged_case(name, seed=seed, num_reqs=16, qlen_range=(512, 4096),
                                 ctx_range=(8192, 65536), num_q_heads=6, num_kv_heads=1,

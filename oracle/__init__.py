@@ -21,19 +21,23 @@ definitions outside this package (dense float64 attention in torch, mpmath
 brute force, closed forms, Python-set semantics, numpy reshapes); none is
 "parity unpinned".
 """
-from .attention import bf16_to_f64, sparse_attention, chunk_prefill, row_attention
+from .attention import bf16_to_f64, kv_rows_f64, sparse_attention, chunk_prefill, row_attention
 from .union import union_build, union_attention, chunk_union_build, chunk_union_attention
 from .pages import page_mark, page_split
+from .fp8 import fp8_e4m3_to_f64, mla_fp8_rows_to_f64
 
 __all__ = [
     "bf16_to_f64",
     "sparse_attention",
     "chunk_prefill",
     "row_attention",
+    "kv_rows_f64",
     "union_build",
     "union_attention",
     "chunk_union_build",
     "chunk_union_attention",
+    "fp8_e4m3_to_f64",
+    "mla_fp8_rows_to_f64",
     "page_mark",
     "page_split",
 ]

@@ -41,6 +41,14 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
         return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def kv_rows_f64(rows: np.ndarray) -> np.ndarray:
+    """K/V rows as float64: bf16 bit patterns (uint16) are widened exactly;
+    rows already decoded to float64 (the FP8 MLA rows, see fp8.py) pass
+    through."""
+    rows = np.asarray(rows)
+    return rows if rows.dtype == np.float64 else bf16_to_f64(rows)
+
+
 def row_attention(q_heads: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray,
                   scale: float) -> Tuple[np.ndarray, np.ndarray]:
     """Softmax attention of a few query heads over an explicit list of rows.
@@ -99,8 +107,8 @@ def sparse_attention(q: np.ndarray, k: np.ndarray, v: Optional[np.ndarray],
         limit = None if topk_len is None else int(topk_len[t])
         tok = _valid_slots(idx[t], kv_len, limit)
         for kvh in range(num_kv_heads):
-            kr = bf16_to_f64(k[tok, kvh, :])
-            vr = kr[:, :dv] if v is None else bf16_to_f64(v[tok, kvh, :])
+            kr = kv_rows_f64(k[tok, kvh, :])
+            vr = kr[:, :dv] if v is None else kv_rows_f64(v[tok, kvh, :])
             heads = slice(kvh * group, (kvh + 1) * group)
             o, s = row_attention(bf16_to_f64(q[t, heads, :]), kr, vr, scale)
             out[r, heads] = o

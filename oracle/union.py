@@ -28,7 +28,7 @@ from typing import Tuple
 
 import numpy as np
 
-from .attention import bf16_to_f64, row_attention
+from .attention import bf16_to_f64, kv_rows_f64, row_attention
 
 
 def union_build(idx: np.ndarray, kv_len: int, G: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
@@ -81,8 +81,8 @@ def union_attention(q: np.ndarray, k: np.ndarray, v, union_idx: np.ndarray,
         own = (union_bits[g, :n] >> j) & 1
         tok = union_idx[g, :n][own.astype(bool)].astype(np.int64)
         for kvh in range(num_kv_heads):
-            kr = bf16_to_f64(k[tok, kvh, :])
-            vr = kr[:, :dv] if v is None else bf16_to_f64(v[tok, kvh, :])
+            kr = kv_rows_f64(k[tok, kvh, :])
+            vr = kr[:, :dv] if v is None else kv_rows_f64(v[tok, kvh, :])
             heads = slice(kvh * group, (kvh + 1) * group)
             o, s = row_attention(bf16_to_f64(q[t, heads, :]), kr, vr, scale)
             out[r, heads] = o

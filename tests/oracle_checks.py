@@ -339,6 +339,50 @@ def check_chunk_union_equals_per_token(chunk_union_build, chunk_union_attention,
 
 
 # --------------------------------------------------------------------------
+# FP8 MLA records
+
+def check_fp8_decode(fp8_e4m3_to_f64):
+    """Every E4M3 code against torch's float8_e4m3fn widening (a library
+    routine: OCP e4m3fn, bias 7, NaN at S.1111.111, no infinities)."""
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = fp8_e4m3_to_f64(codes)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan), "fp8 NaN codes"
+    assert np.array_equal(got[~nan], want[~nan]), "fp8 values"
+
+
+def check_mla_fp8_rows(mla_fp8_rows_to_f64):
+    """Hand-built records: a different scale per 128-value block, known
+    codes at block edges, known bf16 rope values."""
+    rows = np.zeros((2, 656), np.uint8)
+    scales = np.array([[0.5, 3.0, -0.25, 1e-3], [2.0, 4.0, 8.0, 16.0]], dtype="<f4")
+    rows[:, 512:528] = scales.view(np.uint8)
+    for b in range(4):
+        rows[0, 128 * b] = 0x38          # 1.0
+        rows[0, 128 * b + 127] = 0xC0    # -2.0
+    rows[1, 5] = 0x01                    # 2^-9, subnormal
+    rows[1, 300] = 0x7E                  # 448
+    rope = np.array([1.5, -0.75, 0.0, 3.0], dtype=np.float32)
+    rb = (rope.view(np.uint32) >> 16).astype("<u2")
+    rows[0, 528:536] = rb.view(np.uint8)
+    rows[1, 648:656] = rb.view(np.uint8)
+    d = mla_fp8_rows_to_f64(rows)
+    assert d.shape == (2, 576)
+    want0 = np.zeros(576)
+    for b in range(4):
+        want0[128 * b] = float(scales[0, b])
+        want0[128 * b + 127] = -2.0 * float(scales[0, b])
+    want0[512:516] = rope
+    want1 = np.zeros(576)
+    want1[5] = 2.0 ** -9 * 2.0
+    want1[300] = 448.0 * 8.0
+    want1[572:576] = rope
+    assert np.array_equal(d[0], want0), "record 0"
+    assert np.array_equal(d[1], want1), "record 1"
+
+
+# --------------------------------------------------------------------------
 # pages
 
 def check_page_mark(page_mark, seed=9):

@@ -341,3 +341,50 @@ def _loose_build(idx, cu_q, cu_kv, G):
         ui, ub, ul = oracle.union_build(idx[q0:q1], int(cu_kv[-1]), G)
         parts.append((ui, ub, ul, np.full(len(ul), r, np.int32)))
     return tuple(np.concatenate([p[i] for p in parts]) for i in range(4))
+
+
+# FP8 MLA records ----------------------------------------------------------
+
+def test_fp8_decode():
+    C.check_fp8_decode(oracle.fp8_e4m3_to_f64)
+
+
+def test_mla_fp8_rows():
+    C.check_mla_fp8_rows(oracle.mla_fp8_rows_to_f64)
+
+
+def _fnuz(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e, m = (c >> 3) & 0xF, (c & 7).astype(np.float64)
+    v = np.where(e == 0, m / 8 * 2.0 ** -7, (1 + m / 8) * np.exp2(e - 8.0))
+    return np.where(c & 0x80, -v, v)
+
+
+def test_pins_catch_fp8_mistakes():
+    assert _fails_some([lambda: C.check_fp8_decode(_fnuz)])
+    from oracle import fp8 as F
+
+    def blocks64(rows):
+        r = np.ascontiguousarray(rows)
+        lat = F.fp8_e4m3_to_f64(r[..., :512])
+        sc = r[..., 512:528].copy().view("<f4").astype(np.float64)
+        lat = lat * np.tile(np.repeat(sc, 64, axis=-1), 2)    # scales per 64 values
+        rope = oracle.bf16_to_f64(r[..., 528:].copy().view("<u2"))
+        return np.concatenate([lat, rope], axis=-1)
+
+    def rope_shift(rows):
+        r = np.ascontiguousarray(rows)
+        lat = F.fp8_e4m3_to_f64(r[..., :512]) * np.repeat(
+            r[..., 512:528].copy().view("<f4").astype(np.float64), 128, axis=-1)
+        rope = oracle.bf16_to_f64(r[..., 512:640].copy().view("<u2"))
+        return np.concatenate([lat, rope], axis=-1)
+
+    def big_endian(rows):
+        r = np.ascontiguousarray(rows)
+        lat = F.fp8_e4m3_to_f64(r[..., :512]) * np.repeat(
+            r[..., 512:528].copy().view(">f4").astype(np.float64), 128, axis=-1)
+        rope = oracle.bf16_to_f64(r[..., 528:].copy().view("<u2"))
+        return np.concatenate([lat, rope], axis=-1)
+
+    for bad in (blocks64, rope_shift, big_endian):
+        assert _fails_some([lambda: C.check_mla_fp8_rows(bad)]), bad.__name__
