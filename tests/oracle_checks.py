@@ -356,7 +356,7 @@ def check_mla_fp8_rows(mla_fp8_rows_to_f64):
     """Hand-built records: a different scale per 128-value block, known
     codes at block edges, known bf16 rope values."""
     rows = np.zeros((2, 656), np.uint8)
-    scales = np.array([[0.5, 3.0, -0.25, 1e-3], [2.0, 4.0, 8.0, 16.0]], dtype="<f4")
+    scales = np.array([[0.5, 3.0, -0.25, 2.0 ** -10], [2.0, 4.0, 8.0, 16.0]], dtype="<f4")
     rows[:, 512:528] = scales.view(np.uint8)
     for b in range(4):
         rows[0, 128 * b] = 0x38          # 1.0
@@ -380,6 +380,19 @@ def check_mla_fp8_rows(mla_fp8_rows_to_f64):
     want1[572:576] = rope
     assert np.array_equal(d[0], want0), "record 0"
     assert np.array_equal(d[1], want1), "record 1"
+    # products that bf16 cannot hold: fp32 product, then nearest-even bf16,
+    # against torch's float8 widening, fp32 multiply and bfloat16 cast
+    rng = np.random.default_rng(13)
+    rows = rng.integers(0, 256, size=(3, 656), dtype=np.uint8)
+    rows[:, :512][(rows[:, :512] & 0x7F) == 0x7F] = 0x3A       # no NaN codes
+    sc = (rng.random((3, 4)) * 3 + 0.01).astype("<f4")
+    rows[:, 512:528] = sc.view(np.uint8)
+    rows[:, 528:] = 0
+    code = torch.from_numpy(rows[:, :512].copy()).view(torch.float8_e4m3fn).float()
+    prod = code * torch.from_numpy(sc).repeat_interleave(128, dim=1)
+    want = prod.to(torch.bfloat16).to(torch.float64).numpy()
+    got = mla_fp8_rows_to_f64(rows)[:, :512]
+    assert np.array_equal(got, want), "fp32 product rounded to bf16"
 
 
 # --------------------------------------------------------------------------

@@ -386,5 +386,12 @@ def test_pins_catch_fp8_mistakes():
         rope = oracle.bf16_to_f64(r[..., 528:].copy().view("<u2"))
         return np.concatenate([lat, rope], axis=-1)
 
-    for bad in (blocks64, rope_shift, big_endian):
+    def exact_product(rows):
+        r = np.ascontiguousarray(rows)
+        lat = F.fp8_e4m3_to_f64(r[..., :512]) * np.repeat(
+            r[..., 512:528].copy().view("<f4").astype(np.float64), 128, axis=-1)
+        rope = oracle.bf16_to_f64(r[..., 528:].copy().view("<u2"))
+        return np.concatenate([lat, rope], axis=-1)
+
+    for bad in (blocks64, rope_shift, big_endian, exact_product):
         assert _fails_some([lambda: C.check_mla_fp8_rows(bad)]), bad.__name__
