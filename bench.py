@@ -55,7 +55,10 @@ def gathered_bytes(case: gen.AttnCase) -> int:
             kv = case.cu_seqlens_kv[r + 1] - case.cu_seqlens_kv[r]
             blk = case.idx[rows]
             valid += int(((blk >= 0) & (blk < kv)).sum())
-    per_slot = case.head_dim_qk * 2 + (0 if case.v_in_k else case.head_dim_v * 2)
+    if case.k.dtype == np.uint8:                     # FP8 MLA records
+        per_slot = case.k.shape[2]
+    else:
+        per_slot = case.head_dim_qk * 2 + (0 if case.v_in_k else case.head_dim_v * 2)
     return valid * case.num_kv_heads * per_slot
 
 
@@ -230,6 +233,26 @@ def measure_others(args, sa, torch, stream):
         res[f"mla_union_G{G}"] = r
         del ws, ui, ub, ul
     del q, k, idx, out, lse
+
+    # MLA over 656-byte FP8 records (dequantised to bf16 as they are staged)
+    c = gen.make_config("C3fp8", args.seed)
+    q = bf16(c.q)
+    k = torch.from_numpy(np.ascontiguousarray(c.k)).cuda()
+    idx = torch.from_numpy(c.idx).cuda()
+    out = torch.empty((c.num_rows, c.num_q_heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((c.num_rows, c.num_q_heads), dtype=torch.float32, device="cuda")
+    ms = _events_ms(torch, stream, lambda: sa.sparse_attn_prefill(
+        q, k, None, idx, sm_scale=c.scale, head_dim_v=512, out=out, lse=lse, stream=stream), w, n)
+    res["mla_fp8_per_token"] = _rate(gathered_bytes(c), ms)
+    res["mla_fp8_per_token"]["speedup_vs_bf16"] = round(res["mla_per_token"]["ms"] / ms, 3)
+    ws = torch.empty(sa.sparse_attn_union_workspace_bytes(c.num_rows, c.topk, 2),
+                     dtype=torch.uint8, device="cuda")
+    ms = _events_ms(torch, stream, lambda: sa.sparse_attn_prefill_union(
+        q, k, None, idx, 2, sm_scale=c.scale, head_dim_v=512, ws=ws, out=out, lse=lse,
+        stream=stream), w, n)
+    res["mla_fp8_union_G2"] = {"ms": round(ms, 4),
+                               "speedup_vs_bf16_union": round(res["mla_union_G2"]["ms"] / ms, 3)}
+    del q, k, idx, out, lse, ws
 
     # ragged chunk prefill, 16 requests
     c = gen.make_config("C4", args.seed)

@@ -51,14 +51,25 @@ typedef enum {
   SA_OK_FALLBACK = 1,
   SA_ERR_NULL = -1,        /* a required pointer is NULL                    */
   SA_ERR_SHAPE = -2,       /* sizes, strides or alignment not acceptable    */
-  SA_ERR_DTYPE = -3,       /* KV dtype other than bf16 (PR 32779,
-                              "Robustness": the wrapper refuses a non-bf16 KV
-                              cache instead of reading packed FP8 bytes)    */
+  SA_ERR_DTYPE = -3,       /* KV dtype not accepted: anything but bf16, or
+                              FP8 records for the 576/512 MLA shape (PR
+                              32779, "Robustness": a packed FP8 pool is
+                              refused, not walked with a bf16 row pitch)   */
   SA_ERR_UNSUPPORTED = -4, /* valid but not built (head dims, group size)   */
   SA_ERR_WORKSPACE = -5,   /* workspace missing or too small                */
   SA_ERR_HIP = -6          /* the HIP runtime reported an error             */
 } sa_status;
 
+/* SA_DTYPE_FP8_E4M3: K rows are 656-byte FP8 MLA records (PR 32320: the
+ * pool's 656-byte FP8 rows; PR 32779, "Accuracy Tests" (c): an FP8-native
+ * kernel reads the pool with its scales), accepted for the (576, 512,
+ * v_in_k) MLA shape only, with kv_row_stride in bytes (>= num_kv_heads *
+ * 656, a multiple of 16). Record layout (the pages do not print it; this
+ * is the reading that accounts for all 656 bytes of a 576-wide row):
+ * bytes 0..511 latent values in OCP FP8 E4M3 (e4m3fn), bytes 512..527 four
+ * little-endian fp32 scales (scale b multiplies latent values 128b ..
+ * 128b+127), bytes 528..655 64 bf16 rope values. The kernel dequantises
+ * each latent value as fp32(code) * scale rounded to bf16. */
 typedef enum { SA_DTYPE_BF16 = 1, SA_DTYPE_FP8_E4M3 = 2 } sa_dtype;
 
 /* Shape of one attention call.

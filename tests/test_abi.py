@@ -64,7 +64,7 @@ def test_validate_ok_shapes():
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(kv_dtype=sa.SA_DTYPE_FP8_E4M3), -3),
+    (dict(kv_dtype=sa.SA_DTYPE_FP8_E4M3), -3),          # FP8 records are MLA-only
     (dict(num_q_heads=7), -2),
     (dict(num_q_heads=0), -2),
     (dict(topk=0), -2),
@@ -211,3 +211,13 @@ def test_chunk_union_workspace_and_host_rejections():
     assert f(ctypes.byref(d), None, None, None, None, None, None, 0, 0, 2, None, 0, None, None,
              None) == 0
     assert sa.sa_call_count("sparse_attn_chunk_prefill_union") == before + 1
+
+
+def test_fp8_records_validation():
+    # 656-byte records for the MLA shape; stride in bytes, multiple of 16
+    d = _mla(kv_dtype=sa.SA_DTYPE_FP8_E4M3, kv_row_stride=656)
+    assert sa.sa_validate_attn(d) == sa.SA_OK
+    assert sa.sa_validate_attn(_mla(kv_dtype=sa.SA_DTYPE_FP8_E4M3, kv_row_stride=672)) == sa.SA_OK
+    assert sa.sa_validate_attn(_mla(kv_dtype=sa.SA_DTYPE_FP8_E4M3, kv_row_stride=648)) == -2
+    assert sa.sa_validate_attn(_mla(kv_dtype=sa.SA_DTYPE_FP8_E4M3, kv_row_stride=664)) == -2
+    assert sa.sa_validate_attn(_mla(kv_dtype=7)) == -3

@@ -1,0 +1,104 @@
+"""GPU parity: MLA over 656-byte FP8 latent records (E4M3 latent values with
+fp32 block scales, bf16 rope) against the fp64 oracle on the decoded rows."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+import top_index_sparse_amd as sa
+from tests.gpu_util import bf16_dev, check_close, config, i32_dev, i64_dev, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _dec(case):
+    return oracle.mla_fp8_rows_to_f64(case.k)          # float64 [kv, 1, 576]
+
+
+def _u8_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _small(seed, T, kv, first, Hq, topk):
+    return gen.make_attn_case("fp8", seed=seed, num_rows=T, kv_len=kv, first_pos=first,
+                              num_q_heads=Hq, num_kv_heads=1, head_dim_qk=576, head_dim_v=512,
+                              topk=topk, v_in_k=True, kv_fp8=True)
+
+
+@pytest.mark.parametrize("Hq", [8, 16, 3, 1])
+def test_fp8_small_padding_and_invalid(Hq):
+    say(f"[fp8] MLA records, {Hq} heads: -1 padding, out-of-range, duplicates")
+    c = _small(70 + Hq, 37, 400, 0, Hq, 256)
+    c.idx[5, 3] = 400
+    c.idx[9, 10:20] = c.idx[9, 9]
+    q, k, idx = bf16_dev(c.q), _u8_dev(c.k), i32_dev(c.idx)
+    out, lse = sa.sparse_attn_prefill(q, k, None, idx, sm_scale=c.scale, head_dim_v=512)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_attention(c.q, _dec(c), None, c.idx, num_kv_heads=1, scale=c.scale,
+                                     kv_len=c.kv_len, head_dim_v=512)
+    check_close(out, lse, ro, rl, f"fp8 Hq={Hq}")
+
+
+def test_fp8_padded_record_stride():
+    say("[fp8] records at a 672-byte stride")
+    c = _small(75, 21, 300, 200, 8, 128)
+    kp = torch.zeros((300, 1, 672), dtype=torch.uint8, device="cuda")
+    kp[:, :, :656] = _u8_dev(c.k)
+    out, lse = sa.sparse_attn_prefill(bf16_dev(c.q), kp[:, :, :656], None, i32_dev(c.idx),
+                                      sm_scale=c.scale, head_dim_v=512)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_attention(c.q, _dec(c), None, c.idx, num_kv_heads=1, scale=c.scale,
+                                     kv_len=c.kv_len, head_dim_v=512)
+    check_close(out, lse, ro, rl, "fp8 stride 672")
+
+
+def test_fp8_c3_per_token_and_union():
+    say("[fp8] C3fp8 full size: per-token and union G=2/4, sampled rows")
+    c = config("C3fp8")
+    kd = _dec(c)
+    q, k, idx = bf16_dev(c.q), _u8_dev(c.k), i32_dev(c.idx)
+    rows = sample_rows(c.num_rows, 32)
+    sel = torch.from_numpy(rows).cuda()
+    ro, rl = oracle.sparse_attention(c.q, kd, None, c.idx, num_kv_heads=1, scale=c.scale,
+                                     kv_len=c.kv_len, head_dim_v=512, rows=rows)
+    po, pl = sa.sparse_attn_prefill(q, k, None, idx, sm_scale=c.scale, head_dim_v=512)
+    torch.cuda.synchronize()
+    e, el = check_close(po[sel], pl[sel], ro, rl, "C3fp8 per-token")
+    say(f"  per-token: max abs err O {e:.2e} LSE {el:.2e}")
+    for G in (2, 4):
+        uo, ul, st = sa.sparse_attn_prefill_union(q, k, None, idx, G, sm_scale=c.scale,
+                                                  head_dim_v=512)
+        torch.cuda.synchronize()
+        assert st == sa.SA_OK
+        check_close(uo[sel], ul[sel], ro, rl, f"C3fp8 union G={G}")
+        assert (ul - pl).abs().max().item() < 2e-5
+        assert ((uo - po).abs() <= 2e-2 + 1e-2 * po.abs()).all()
+
+
+def test_fp8_ragged_chunk_prefill():
+    say("[fp8] ragged chunk prefill over FP8 records, per-token and union G=2")
+    rng = np.random.default_rng(77)
+    qlens, ctxs = [9, 0, 14, 5], [700, 100, 900, 300]
+    cu_q = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    cu_kv = np.concatenate([[0], np.cumsum(ctxs)]).astype(np.int64)
+    T, KV = int(cu_q[-1]), int(cu_kv[-1])
+    q = gen.normal_bf16(rng, (T, 8, 576))
+    k = gen.mla_fp8_rows(rng, KV).reshape(KV, 1, 656)
+    idx = np.concatenate([gen.random_walk_indices(rng, np.arange(c - n, c), 256, swap_frac=0.1)
+                          for n, c in zip(qlens, ctxs)]).astype(np.int32)
+    scale = 1 / 24
+    dq, dk, di = bf16_dev(q), _u8_dev(k), i32_dev(idx)
+    dcq, dck = i32_dev(cu_q), i64_dev(cu_kv)
+    kd = oracle.mla_fp8_rows_to_f64(k)
+    ro, rl = oracle.chunk_prefill(q, kd, None, idx, cu_q, cu_kv, num_kv_heads=1, scale=scale,
+                                  head_dim_v=512)
+    out, lse = sa.sparse_attn_chunk_prefill(dq, dk, None, di, dcq, dck, sm_scale=scale,
+                                            head_dim_v=512)
+    torch.cuda.synchronize()
+    check_close(out, lse, ro, rl, "fp8 ragged")
+    uo, ul, st = sa.sparse_attn_chunk_prefill_union(dq, dk, None, di, dcq, dck, 2, sm_scale=scale,
+                                                    head_dim_v=512)
+    torch.cuda.synchronize()
+    assert st == sa.SA_OK
+    check_close(uo, ul, ro, rl, "fp8 ragged union")

@@ -181,13 +181,17 @@ def _rows_dense(t: torch.Tensor, name: str):
             raise ValueError(f"{name}: every row must be contiguous")
 
 
+FP8_RECORD_BYTES = 656   # 512 E4M3 latent values, 4 fp32 block scales, 64 bf16 rope
+
+
 def _kv_dtype_code(t: torch.Tensor) -> int:
+    """bf16 K/V, or FP8 MLA records given as uint8 [tokens, Hkv, 656]."""
     if t.dtype == torch.bfloat16:
         return SA_DTYPE_BF16
-    fp8 = getattr(torch, "float8_e4m3fn", None)
-    if fp8 is not None and t.dtype == fp8:
+    if t.dtype == torch.uint8 and t.dim() == 3 and t.shape[2] == FP8_RECORD_BYTES:
         return SA_DTYPE_FP8_E4M3
-    raise TypeError(f"K/V dtype {t.dtype} is not supported (bf16 only)")
+    raise TypeError(f"K dtype {t.dtype} / shape {tuple(t.shape)} is not supported "
+                    "(bf16, or uint8 [tokens, Hkv, 656] FP8 MLA records)")
 
 
 def make_desc(q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor], idx: torch.Tensor,

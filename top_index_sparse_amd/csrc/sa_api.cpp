@@ -31,13 +31,16 @@ sa_status ok(sa_entry e, sa_status st = SA_OK) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-enum class Kernel { kNone, kGqa256, kMla576 };
+enum class Kernel { kNone, kGqa256, kMla576, kMla576Fp8 };
+
+constexpr int64_t kFp8RecordBytes = 656;   // 512 E4M3 + 4 fp32 scales + 64 bf16
 
 // Which built kernel serves this descriptor (no pointer checks).
 sa_status check_desc(const sa_attn_desc* d, int32_t G, Kernel* kernel) {
   if (!d) return fail(SA_ERR_NULL, "desc is NULL");
-  if (d->kv_dtype != SA_DTYPE_BF16)
-    return fail(SA_ERR_DTYPE, "kv_dtype %d: only bf16 K/V is accepted", d->kv_dtype);
+  if (d->kv_dtype != SA_DTYPE_BF16 && d->kv_dtype != SA_DTYPE_FP8_E4M3)
+    return fail(SA_ERR_DTYPE, "kv_dtype %d: bf16 K/V, or FP8 MLA records, only", d->kv_dtype);
+  const bool fp8 = d->kv_dtype == SA_DTYPE_FP8_E4M3;
   if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->num_q_heads % d->num_kv_heads != 0)
     return fail(SA_ERR_SHAPE, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
                 d->num_q_heads, d->num_kv_heads);
@@ -51,12 +54,14 @@ sa_status check_desc(const sa_attn_desc* d, int32_t G, Kernel* kernel) {
   if (d->head_dim_qk == 256 && d->head_dim_v == 256 && !d->v_in_k) {
     *kernel = Kernel::kGqa256;
   } else if (d->head_dim_qk == 576 && d->head_dim_v == 512 && d->v_in_k) {
-    *kernel = Kernel::kMla576;
+    *kernel = fp8 ? Kernel::kMla576Fp8 : Kernel::kMla576;
   } else {
     return fail(SA_ERR_UNSUPPORTED,
                 "head dims (%d, %d, v_in_k=%d) not built; built: (256, 256, 0), (576, 512, 1)",
                 d->head_dim_qk, d->head_dim_v, d->v_in_k);
   }
+  if (fp8 && *kernel != Kernel::kMla576Fp8)
+    return fail(SA_ERR_DTYPE, "FP8 K is accepted as 656-byte MLA records (576/512, v_in_k) only");
   if (group > 16) return fail(SA_ERR_UNSUPPORTED, "group %d > 16 query heads per KV head", group);
   const int64_t qrow = (int64_t)d->num_q_heads * d->head_dim_qk;
   const int64_t krow = (int64_t)d->num_kv_heads * d->head_dim_qk;
@@ -66,7 +71,13 @@ sa_status check_desc(const sa_attn_desc* d, int32_t G, Kernel* kernel) {
     return fail(SA_ERR_SHAPE, "q_row_stride %lld: needs >= %lld and a multiple of 8",
                 (long long)d->q_row_stride, (long long)qrow);
   // Row byte strides are 32-bit multipliers in the kernels' address math.
-  if (d->kv_row_stride < krow || d->kv_row_stride % 8 || d->kv_row_stride >= (int64_t)1 << 31)
+  if (fp8) {
+    // records: kv_row_stride counts bytes
+    const int64_t rec = (int64_t)d->num_kv_heads * kFp8RecordBytes;
+    if (d->kv_row_stride < rec || d->kv_row_stride % 16 || d->kv_row_stride >= (int64_t)1 << 32)
+      return fail(SA_ERR_SHAPE, "kv_row_stride %lld bytes: needs >= %lld, a multiple of 16, < 2^32",
+                  (long long)d->kv_row_stride, (long long)rec);
+  } else if (d->kv_row_stride < krow || d->kv_row_stride % 8 || d->kv_row_stride >= (int64_t)1 << 31)
     return fail(SA_ERR_SHAPE, "kv_row_stride %lld: needs >= %lld, a multiple of 8, < 2^31",
                 (long long)d->kv_row_stride, (long long)krow);
   if (!d->v_in_k &&
@@ -105,8 +116,11 @@ sa::AttnParams make_params(const sa_attn_desc* d, const void* q, const void* k, 
   p.out = out;
   p.lse = lse;
   p.q_row_stride = d->q_row_stride;
-  p.k_row_stride = d->kv_row_stride;
-  p.v_row_stride = d->v_in_k ? d->kv_row_stride : d->v_row_stride;
+  // in 2-byte units (the kernels' byte stride is twice this); FP8 record
+  // strides are given in bytes and are even
+  const int64_t kstride = d->kv_dtype == SA_DTYPE_FP8_E4M3 ? d->kv_row_stride / 2 : d->kv_row_stride;
+  p.k_row_stride = kstride;
+  p.v_row_stride = d->v_in_k ? kstride : d->v_row_stride;
   p.idx_row_stride = d->idx_row_stride;
   p.out_row_stride = d->out_row_stride;
   p.num_rows = num_rows;
@@ -127,6 +141,9 @@ sa_status launch_attention(Kernel kernel, const sa::AttnParams& p, int union_mod
       break;
     case Kernel::kMla576:
       e = sa::launch_attn_mla576(p, union_mode, s);
+      break;
+    case Kernel::kMla576Fp8:
+      e = sa::launch_attn_mla576_fp8(p, union_mode, s);
       break;
     default:
       return fail(SA_ERR_UNSUPPORTED, "no kernel for this head-dim combination");

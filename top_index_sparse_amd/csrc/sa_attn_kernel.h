@@ -79,7 +79,7 @@ constexpr float kSlack = 8.f;
 // slot tile adds at most 3 x 16.
 constexpr int kQueueCap = 64;
 
-template <int DQK, int DV, bool V_IN_K, int MODE, int C, int WSPLIT>
+template <int DQK, int DV, bool V_IN_K, int MODE, int C, int WSPLIT, bool FP8>
 struct AttnTile {
   static constexpr int KSTEPS = DQK / 32 / WSPLIT;   // this wave's k-steps of S^T
   static constexpr int VCH = DV / 128 / WSPLIT;      // this wave's 16-byte V chunks per slot
@@ -98,6 +98,9 @@ struct AttnTile {
   static constexpr bool KLDS = !VKLDS && KSTEPS % 4 == 0;
   static_assert(KLDS || VKLDS, "K is staged through LDS");
   static_assert(!V_IN_K || VKLDS, "V inside K is read from the staged K slice");
+  // FP8: K rows are 656-byte records (512 E4M3 latent values, four fp32
+  // block scales, 64 bf16 rope values), dequantised into the same bf16 slice
+  static_assert(!FP8 || (VKLDS && DQK == 576 && DV == 512 && WSPLIT == 2), "FP8 records");
   static constexpr int KCH = KLDS ? KSTEPS / 4 : 0;   // 16-byte K chunks per slot per lane
   static constexpr int KROW = 64 * KSTEPS + 16;       // LDS row pitch (bytes): 16 (mod 32) * odd
   static constexpr int KLDS_BYTES = 16 * KROW;
@@ -112,11 +115,11 @@ struct AttnTile {
 
 // Team `team_id`, wavefront `split` of WSPLIT. xch: partial-score exchange
 // [2][WG_WAVES][C][64]; klds: per-wave K tiles; qtok/qbits: per-wave queues.
-template <int DQK, int DV, bool V_IN_K, int MODE, int C, int WSPLIT>
+template <int DQK, int DV, bool V_IN_K, int MODE, int C, int WSPLIT, bool FP8>
 __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int split,
                                           f32x4_t* xch, uint8_t* klds, int32_t* qtok_all,
                                           uint32_t* qbits_all) {
-  using TT = AttnTile<DQK, DV, V_IN_K, MODE, C, WSPLIT>;
+  using TT = AttnTile<DQK, DV, V_IN_K, MODE, C, WSPLIT, FP8>;
   constexpr int KSTEPS = TT::KSTEPS;
   constexpr int VCH = TT::VCH;
   constexpr int MTILES = TT::MTILES;
@@ -301,7 +304,9 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   // which are multiplied by p = 0.
   const uint32_t k_row_bytes = (uint32_t)(2 * p.k_row_stride);   // < 2^32 (host check)
   const uint32_t v_row_bytes = (uint32_t)(2 * p.v_row_stride);
-  const uint8_t* kwb = reinterpret_cast<const uint8_t*>(kw);
+  // FP8 records: kvh's record of row 0 (k_row_stride counts 2-byte units)
+  const uint8_t* kwb = FP8 ? reinterpret_cast<const uint8_t*>(p.k) + team_kv * k_row_bytes + kvh * 656
+                           : reinterpret_cast<const uint8_t*>(kw);
   const uint8_t* kbn = kwb + 16 * n;   // this lane's 16 bytes of a 256-byte half row
   const uint8_t* vbn = reinterpret_cast<const uint8_t*>(vw) + 16 * n;
   // Issues a tile's loads; returns the score masks: bit i of mask[c] set
@@ -318,6 +323,22 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
 #pragma unroll
       for (int i = 0; i < 4; ++i) mk |= (uint32_t)(khi[i] >= 0 && ((uint32_t)bq[i] & col_bit[c])) << i;
       mask[c] = mk;
+    }
+    if constexpr (FP8) {
+      // Per slot 4g+i: the wave's 256 latent bytes, sixteen lanes per row.
+      // Per lane: one rope chunk (slot 4g + n/4, chunk n%4 of the wave's 64
+      // rope bytes) and the 16 scale bytes of slot 4g + n%4.
+      int klo[4];
+      row_bcast4((int)koff, klo);
+      const int ir = n >> 2, is = n & 3;
+      auto pick = [](const int a[4], int i) { return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3]; };
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (khi[i] >= 0) td.kd[i] = ld16(kwb + join64(klo[i], khi[i]) + 256 * split + 16 * n);
+      const int rhi = pick(khi, ir), shi = pick(khi, is);
+      if (rhi >= 0) td.kd[4] = ld16(kwb + join64(pick(klo, ir), rhi) + 528 + 64 * split + 16 * is);
+      if (shi >= 0) td.kd[5] = ld16(kwb + join64(pick(klo, is), shi) + 512);
+      return;
     }
     if (VKLDS) {
       // Linear chunk order: load q covers chunks 64q .. 64q+63 of the tile's
@@ -372,7 +393,31 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   uint8_t* lk = klds + wv * TT::KLDS_BYTES;   // this wave's K tile in LDS
   auto compute = [&](const Data& td, const uint32_t mask[C]) {
     // Stage the gathered rows in LDS, in the A-operand order.
-    if (VKLDS) {
+    if constexpr (FP8) {
+      // Dequantise: latent chunk n of slot 4g+i (values 16n .. 16n+15 of the
+      // wave's slice, block 2 split + n/8) times its block scale, rounded to
+      // bf16, becomes slice chunks 2n and 2n+1; the rope chunk is bf16
+      // already. The scales of slot 4g+i sit in quad lane i.
+      int s0[4], s1[4];
+      quad_bcast4((int)td.kd[5][2 * split], s0);
+      quad_bcast4((int)td.kd[5][2 * split + 1], s1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sc = __builtin_bit_cast(float, (n >> 3) ? s1[i] : s0[i]);
+        uint32_t b[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)td.kd[i][w], false);
+          const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)td.kd[i][w], true);
+          b[2 * w] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
+          b[2 * w + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
+        }
+        uint8_t* row = lk + (4 * g + i) * KROW + 32 * n;
+        *reinterpret_cast<u32x4_t*>(row) = (u32x4_t){b[0], b[1], b[2], b[3]};
+        *reinterpret_cast<u32x4_t*>(row + 16) = (u32x4_t){b[4], b[5], b[6], b[7]};
+      }
+      *reinterpret_cast<u32x4_t*>(lk + (4 * g + (n >> 2)) * KROW + 16 * (MAIN / 8 + (n & 3))) = td.kd[4];
+    } else if (VKLDS) {
 #pragma unroll
       for (int q = 0; q < KSTEPS; ++q) {
         const int e = 64 * q + lane;
@@ -544,21 +589,21 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
 
 // WSPLIT = 1: four independent one-wave teams per workgroup. WSPLIT = 2:
 // one team per workgroup, its two halves exchanging partial scores.
-template <int DQK, int DV, bool V_IN_K, int MODE, int C, int WSPLIT, int WAVES>
+template <int DQK, int DV, bool V_IN_K, int MODE, int C, int WSPLIT, bool FP8, int WAVES>
 __global__ void __attribute__((amdgpu_flat_work_group_size(64, 256),
                                amdgpu_waves_per_eu(WAVES, WAVES)))
 attn_kernel(AttnParams p) {
-  using TT = AttnTile<DQK, DV, V_IN_K, MODE, C, WSPLIT>;
+  using TT = AttnTile<DQK, DV, V_IN_K, MODE, C, WSPLIT, FP8>;
   __shared__ f32x4_t xch[WSPLIT > 1 ? 2 * TT::WG_WAVES * C * 64 : 1];
   __shared__ __attribute__((aligned(16))) uint8_t klds[TT::WG_WAVES * TT::KLDS_BYTES];
   __shared__ int32_t qtok[MODE == kUnion ? 1 : TT::WG_WAVES * kQueueCap];
   __shared__ uint32_t qbits[MODE == kUnion ? 1 : TT::WG_WAVES * kQueueCap];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (WSPLIT == 1)
-    attn_team<DQK, DV, V_IN_K, MODE, C, 1>(p, bid * 4 + w, 0, xch, klds, qtok, qbits);
+  if constexpr (WSPLIT == 1)
+    attn_team<DQK, DV, V_IN_K, MODE, C, 1, FP8>(p, bid * 4 + w, 0, xch, klds, qtok, qbits);
   else
-    attn_team<DQK, DV, V_IN_K, MODE, C, WSPLIT>(p, bid, w, xch, klds, qtok, qbits);
+    attn_team<DQK, DV, V_IN_K, MODE, C, WSPLIT, FP8>(p, bid, w, xch, klds, qtok, qbits);
 }
 
 // Workgroups and threads per workgroup for a launch.

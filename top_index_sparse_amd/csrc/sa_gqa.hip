@@ -11,7 +11,7 @@ template <int MODE, int C, int WSPLIT>
 void launch(const AttnParams& p, hipStream_t stream) {
   dim3 grid, block;
   attn_grid<WSPLIT>(p, MODE, &grid, &block);
-  hipLaunchKernelGGL((attn_kernel<256, 256, false, MODE, C, WSPLIT, 2>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((attn_kernel<256, 256, false, MODE, C, WSPLIT, false, 2>), grid, block, 0, stream, p);
 }
 
 // One wave with whole K/V rows for 16 columns; two waves, each with half of

@@ -104,6 +104,7 @@ struct PageParams {
 // launchers choose the team shape (rows per team, column tiles).
 hipError_t launch_attn_gqa256(AttnParams p, int union_mode, hipStream_t stream);
 hipError_t launch_attn_mla576(AttnParams p, int union_mode, hipStream_t stream);
+hipError_t launch_attn_mla576_fp8(AttnParams p, int union_mode, hipStream_t stream);
 hipError_t launch_union_build(const UnionBuildParams& p, hipStream_t stream);
 // Ragged: writes gstart[0..num_reqs] from cu_q, then builds every group's
 // union over its request's KV range with bit planes.
