@@ -299,6 +299,8 @@ class PageCase:
            rows of row_bytes, then src_page_tokens scales of scale_bytes
     idx    int32 [batch, topk] pool token ids (page * src_page_tokens + slot),
            -1 padding
+    q      bf16 bits [batch, num_q_heads, 576]: the decode step's MLA queries
+           (None for a pool of bytes only)
     """
     name: str
     src: np.ndarray
@@ -307,6 +309,8 @@ class PageCase:
     dst_page_tokens: int
     row_bytes: int
     scale_bytes: int
+    q: Optional[np.ndarray] = None
+    scale: float = 1.0 / 24.0
 
     @property
     def num_src_pages(self) -> int:
@@ -325,21 +329,31 @@ class PageCase:
         return self.src_page_tokens // self.dst_page_tokens
 
     def arrays(self) -> Dict[str, np.ndarray]:
-        return {"src": self.src, "idx": self.idx}
+        out = {"src": self.src, "idx": self.idx}
+        if self.q is not None:
+            out["q"] = self.q
+        return out
 
 
 def make_page_case(name: str, *, seed: int, num_src_pages: int = 4096,
                    src_page_tokens: int = 256, dst_page_tokens: int = 64,
                    row_bytes: int = 656, scale_bytes: int = 4, batch: int = 32,
-                   topk: int = 2048, window: int = 256, spread: bool = False) -> PageCase:
-    """Pool of random bytes plus one decode step's indices.
+                   topk: int = 2048, window: int = 256, spread: bool = False,
+                   num_q_heads: int = 8) -> PageCase:
+    """Pool of random bytes plus one decode step's indices and queries.
 
     Each request owns its own pool pages (a random page table, disjoint across
     requests). Default: its slots hold the pool ids of its last `window`
     tokens, then -1, so about two pages per request are touched. With
     spread=True its topk slots are distinct positions spread over its whole
-    context (a stress case that touches many pages)."""
-    _, _, _, ri, rl, rp = _streams(seed)
+    context (a stress case that touches many pages).
+
+    With 656-byte rows the token rows that the indices reference are
+    overwritten with FP8 MLA records (mla_fp8_rows), and q holds batch x
+    num_q_heads bf16 N(0,1) queries of width 576, so the step can also be
+    attended; every other byte of the pool, the per-token scale words
+    included, stays random."""
+    rq, rk, _, ri, rl, rp = _streams(seed)
     page_bytes = src_page_tokens * (row_bytes + scale_bytes)
     src = rp.integers(0, 256, size=(num_src_pages, page_bytes), dtype=np.uint8)
     pages_per_req = num_src_pages // batch
@@ -356,7 +370,15 @@ def make_page_case(name: str, *, seed: int, num_src_pages: int = 4096,
             pos = np.arange(ctx - n, ctx)
         page = perm[b, pos // src_page_tokens]
         idx[b, :n] = (page * src_page_tokens + pos % src_page_tokens).astype(np.int32)
-    return PageCase(name, src, idx, src_page_tokens, dst_page_tokens, row_bytes, scale_bytes)
+    q = None
+    if row_bytes == FP8_ROW_BYTES:
+        tok = np.unique(idx[idx >= 0]).astype(np.int64)
+        rec = mla_fp8_rows(rk, len(tok))
+        page, slot = tok // src_page_tokens, tok % src_page_tokens
+        cols = slot[:, None] * row_bytes + np.arange(row_bytes)[None, :]
+        src[page[:, None], cols] = rec
+        q = normal_bf16(rq, (batch, num_q_heads, 576))
+    return PageCase(name, src, idx, src_page_tokens, dst_page_tokens, row_bytes, scale_bytes, q)
 
 
 CONFIG_NAMES = ("C0a", "C0b", "C1", "C2", "C3", "C3tail", "C3fp8", "C4", "C4decode",
@@ -382,7 +404,8 @@ def make_config(name: str, seed: int = 0):
     C4   16 ragged requests, qlen and context log-uniform in [512, 4096] and
          [8192, 65536], group 6 / one KV head, d 256, top-k 2051 walk
     C4decode  4096-page pool of 256-token pages (656 B rows plus 4 B scales),
-         batch 32 x 2048 indices over each request's last 256 tokens
+         batch 32 x 2048 indices over each request's last 256 tokens (the
+         referenced rows are FP8 MLA records), 8 MLA query heads per request
     C4spread  the same pool with 2048 indices spread over each context
     """
     if name == "C0a":

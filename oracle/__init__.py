@@ -12,6 +12,8 @@ attention   per-token sparse attention and ragged chunk prefill
 union       union-of-G index build (sorted, deduplicated, ownership bits) and
             union attention
 pages       decode-pool page mark and (masked) page split
+fp8         the 656-byte FP8 MLA record and its dequantisation to bf16
+decode      sparse MLA decode over the split pages of FP8 records
 
 Every function cites the passage of the pages it restates. Where the pages
 leave a point open, the reading taken is stated at the function.
@@ -25,6 +27,7 @@ from .attention import bf16_to_f64, kv_rows_f64, sparse_attention, chunk_prefill
 from .union import union_build, union_attention, chunk_union_build, chunk_union_attention
 from .pages import page_mark, page_split
 from .fp8 import fp8_e4m3_to_f64, mla_fp8_rows_to_f64
+from .decode import paged_decode, paged_record
 
 __all__ = [
     "bf16_to_f64",
@@ -38,6 +41,8 @@ __all__ = [
     "chunk_union_attention",
     "fp8_e4m3_to_f64",
     "mla_fp8_rows_to_f64",
+    "paged_decode",
+    "paged_record",
     "page_mark",
     "page_split",
 ]

@@ -431,3 +431,84 @@ def check_page_split(page_split, seed=10):
             assert np.array_equal(part[d], full[d]), "masked = full on touched"
         else:
             assert np.all(part[d] == 0xA5), "untouched stays stale"
+
+
+# --------------------------------------------------------------------------
+# sparse MLA decode over split pages
+
+def _record(value_scale):
+    """A 656-byte FP8 record whose 512 latent values all equal value_scale
+    (code 0x38 = 1.0 times the scale in every block) and whose rope is 0."""
+    r = np.zeros(656, np.uint8)
+    r[:512] = 0x38
+    r[512:528] = np.full(4, value_scale, dtype="<f4").view(np.uint8)
+    return r
+
+
+def check_paged_decode_closed_form(paged_decode):
+    """Two 64-token pages, token t's latent values all t + 1: mean values,
+    log-counts and a softmax over known scores, in closed form."""
+    rng = np.random.default_rng(21)
+    ptok, stride = 64, 64 * 660 + 32                   # rows, per-token words, padding
+    pool = rng.integers(0, 256, size=(2, stride), dtype=np.uint8)   # garbage elsewhere
+    for t in (0, 5, 64, 70, 127):
+        p, r = divmod(t, ptok)
+        pool[p, r * 656:(r + 1) * 656] = _record(t + 1.0)
+    q = np.zeros((3, 2, 576), np.uint16)
+    q[1, 0, 3] = 0x3F80                                # head 0 reads latent dim 3
+    q[1, 1, 560] = 0x3F80                              # head 1 reads a rope dim (0)
+    idx = np.array([[5, 70, -1, 5, 128, -7],
+                    [0, 127, 64, -1, -1, -1],
+                    [-1, -1, -1, -1, -1, -1]], np.int32)
+    scale = 0.05
+    o, lse = paged_decode(q, pool, idx, page_tokens=ptok, scale=scale)
+    assert o.shape == (3, 2, 512) and lse.shape == (3, 2)
+    # request 0: zero query, multiset {6, 71, 6}
+    assert np.allclose(o[0], (6 + 71 + 6) / 3, rtol=0, atol=1e-12), "mean over the multiset"
+    assert np.allclose(lse[0], math.log(3), rtol=0, atol=1e-12), "log count"
+    # request 1, head 0: scores scale * (t + 1) over {1, 128, 65}
+    vals = [1.0, 128.0, 65.0]
+    w = [math.exp(scale * x) for x in vals]
+    assert np.allclose(o[1, 0], sum(a * b for a, b in zip(w, vals)) / sum(w), rtol=0, atol=1e-10)
+    assert abs(lse[1, 0] - math.log(sum(w))) < 1e-12, "softmax lse"
+    assert np.allclose(o[1, 1], sum(vals) / 3, rtol=0, atol=1e-12), "rope-only head"
+    assert np.all(o[2] == 0) and np.all(np.isneginf(lse[2])), "empty support"
+    # topk_len: request 0 sees {6, 71}, request 1 nothing past slot 0
+    o, lse = paged_decode(q, pool, idx, page_tokens=ptok, scale=scale,
+                          topk_len=np.array([2, 1, 6], np.int32))
+    assert np.allclose(o[0], 38.5, rtol=0, atol=1e-12) and np.allclose(lse[0], math.log(2))
+    assert np.allclose(o[1], 1.0, rtol=0, atol=1e-12), "one slot: its own V"
+
+
+def check_paged_decode_vs_source(paged_decode, sparse_attention, mla_fp8_rows_to_f64, seed=22):
+    """Pages of 64 tokens built from 256-token source pages by numpy
+    reshapes; the decode over them equals per-token sparse attention over
+    the records in token order (the source layout), duplicates, padding,
+    out-of-pool ids and per-request lengths included."""
+    rng = np.random.default_rng(seed)
+    P, stok, dtok, rb, sb = 3, 256, 64, 656, 4
+    tokens = P * stok
+    records = gen.mla_fp8_rows(rng, tokens)
+    words = rng.integers(0, 256, size=(P, stok * sb), dtype=np.uint8)
+    src = np.concatenate([records.reshape(P, stok * rb), words], axis=1)
+    ratio = stok // dtok
+    data = src[:, :stok * rb].reshape(P * ratio, dtok * rb)
+    sc = src[:, stok * rb:].reshape(P * ratio, dtok * sb)
+    pad = np.full((P * ratio, 48), 0xA5, np.uint8)
+    dst = np.concatenate([data, sc, pad], axis=1)
+    B, Hq, k = 5, 4, 40
+    q = gen.normal_bf16(rng, (B, Hq, 576))
+    idx = rng.integers(-4, tokens + 30, size=(B, k)).astype(np.int32)
+    idx[1, 10:20] = idx[1, :10]                      # duplicates
+    idx[2] = -1
+    topk_len = np.array([k, 33, k, 7, 0], np.int32)
+    scale = 1.0 / 24
+    rows = mla_fp8_rows_to_f64(records)[:, None, :]   # [tokens, 1, 576] float64
+    for tl in (None, topk_len):
+        got_o, got_l = paged_decode(q, dst, idx, page_tokens=dtok, scale=scale, topk_len=tl)
+        want_o, want_l = sparse_attention(q, rows, None, idx, num_kv_heads=1, scale=scale,
+                                          kv_len=tokens, head_dim_v=512, topk_len=tl)
+        assert np.allclose(got_o, want_o, rtol=0, atol=1e-12), "decode O"
+        fin = np.isfinite(want_l)
+        assert np.array_equal(fin, np.isfinite(got_l)), "empty rows"
+        assert np.allclose(got_l[fin], want_l[fin], rtol=0, atol=1e-12), "decode LSE"

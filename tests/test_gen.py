@@ -108,6 +108,15 @@ def test_page_case():
     for a in range(32):
         for b in range(a + 1, 32):
             assert not (per_req[a] & per_req[b])
+    # the referenced rows are FP8 records: finite block scales amax/448
+    # (each block's largest code is +-448), no NaN codes; 8 query heads
+    assert c.q.shape == (32, 8, 576) and c.q.dtype == np.uint16
+    tok = np.unique(v)[:50]
+    rec = np.stack([c.src[t // 256, (t % 256) * 656:(t % 256 + 1) * 656] for t in tok])
+    sc = rec[:, 512:528].copy().view("<f4")
+    assert np.all(np.isfinite(sc)) and np.all(sc > 0)
+    assert not np.any((rec[:, :512] & 0x7F) == 0x7F)
+    assert np.all((rec[:, :512].reshape(-1, 4, 128) & 0x7F).max(axis=2) == 0x7E)
 
 
 def test_shuffle_slots_keeps_sets_and_breaks_alignment():

@@ -395,3 +395,69 @@ def test_pins_catch_fp8_mistakes():
 
     for bad in (blocks64, rope_shift, big_endian, exact_product):
         assert _fails_some([lambda: C.check_mla_fp8_rows(bad)]), bad.__name__
+
+
+# sparse MLA decode over split pages ---------------------------------------
+
+def test_paged_decode_closed_form():
+    C.check_paged_decode_closed_form(oracle.paged_decode)
+
+
+def test_paged_decode_vs_source():
+    C.check_paged_decode_vs_source(oracle.paged_decode, oracle.sparse_attention,
+                                   oracle.mla_fp8_rows_to_f64)
+
+
+def _decode_mutant(record, tokens_of=None, dedupe=False):
+    """oracle.paged_decode with its record lookup (or validity bound, or
+    multiplicity) replaced."""
+    from oracle import decode as D
+
+    def run(q, pool, idx, *, page_tokens, scale, topk_len=None, row_bytes=656):
+        B, Hq, _ = q.shape
+        tokens = pool.shape[0] * page_tokens if tokens_of is None else tokens_of(pool, page_tokens)
+        out, lse = np.zeros((B, Hq, 512)), np.zeros((B, Hq))
+        for b in range(B):
+            lim = idx.shape[1] if topk_len is None else max(0, min(int(topk_len[b]), idx.shape[1]))
+            tok = [int(t) for t in idx[b, :lim] if 0 <= t < tokens]
+            if dedupe:
+                tok = sorted(set(tok))
+            rec = np.zeros((len(tok), 656), np.uint8)
+            for i, t in enumerate(tok):
+                rec[i] = record(pool, t, page_tokens)
+            rows = oracle.mla_fp8_rows_to_f64(rec)
+            out[b], lse[b] = oracle.row_attention(oracle.bf16_to_f64(q[b]), rows, rows[:, :512], scale)
+        return out, lse
+    return run
+
+
+def _decode_checks(fn):
+    return [lambda: C.check_paged_decode_closed_form(fn),
+            lambda: C.check_paged_decode_vs_source(fn, oracle.sparse_attention,
+                                                   oracle.mla_fp8_rows_to_f64)]
+
+
+def test_pins_catch_decode_mistakes():
+    def src_pages(pool, t, ptok):             # 256-token source geometry on 64-token pages
+        p, r = divmod(t, 256)
+        return pool[p, r * 656:(r + 1) * 656]
+
+    def pitch660(pool, t, ptok):              # row pitch counts the per-token word
+        p, r = divmod(t, ptok)
+        return pool[p, r * 660:r * 660 + 656]
+
+    def scales_first(pool, t, ptok):          # per-token words before the rows
+        p, r = divmod(t, ptok)
+        return pool[p, ptok * 4 + r * 656:ptok * 4 + (r + 1) * 656]
+
+    def good(pool, t, ptok):
+        return oracle.paged_record(pool, t, page_tokens=ptok)
+
+    mutants = [_decode_mutant(src_pages), _decode_mutant(pitch660), _decode_mutant(scales_first),
+               _decode_mutant(good, dedupe=True),
+               _decode_mutant(good, tokens_of=lambda pool, ptok: pool.shape[0] * 256)]   # source-page bound
+    for m in mutants:
+        assert _fails_some(_decode_checks(m))
+    # the unmutated copy passes, so the mutants fail for their mistake alone
+    for chk in _decode_checks(_decode_mutant(good)):
+        chk()
