@@ -10,7 +10,8 @@
  *   - the same over ragged requests with cached prefixes (chunk prefill);
  *   - union mode: G adjacent rows share one sorted, deduplicated index set
  *     with per-row ownership bits that restore each row's own support;
- *   - the decode-pool page mark and (masked) page split.
+ *   - the decode-pool page mark and (masked) page split;
+ *   - sparse MLA decode over the split pool's FP8 records.
  *
  * Conventions for every entry point:
  *   - Device pointers are owned by the caller. The library allocates and
@@ -98,7 +99,8 @@ typedef struct {
   int32_t head_dim_v;
   int32_t topk;
   int32_t v_in_k;
-  int32_t kv_dtype;  /* sa_dtype; only SA_DTYPE_BF16 is accepted */
+  int32_t kv_dtype;  /* sa_dtype: SA_DTYPE_BF16, or SA_DTYPE_FP8_E4M3 for the
+                        (576, 512, v_in_k) shape (kv_row_stride in bytes) */
   float sm_scale;    /* multiplies q.k before the softmax */
   int64_t q_row_stride;
   int64_t kv_row_stride;
@@ -256,6 +258,46 @@ sa_status page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src_pages,
 sa_status page_split(const sa_page_desc* desc, const uint8_t* src, uint8_t* dst,
                      const int8_t* mask, int32_t num_src_pages, hipStream_t stream);
 
+/* Bytes of device workspace sparse_attn_decode_paged needs (0 on invalid
+ * sizes, and for batch 0). */
+size_t sparse_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t topk);
+
+/* Sparse MLA decode over the split pool (sglang PR 32320: the decode
+ * attention that reads the 64-token pages page_split writes, listed after
+ * the split in its "Accuracy Tests" profile). Request b has one query row,
+ * q[b] (num_q_heads heads of 576 bf16), and top-k pool token ids idx[b]:
+ * token t is the FP8 MLA record at row t % dst_page_tokens of destination
+ * page t / dst_page_tokens (the ids page_mark takes; after the split, row s
+ * of source page p is row s % dst_page_tokens of destination page
+ * p * ratio + s / dst_page_tokens). The result is the per-token sparse
+ * attention of sparse_attn_prefill over those records (dequantised as for
+ * SA_DTYPE_FP8_E4M3), with t valid iff 0 <= t < num_dst_pages *
+ * dst_page_tokens. The per-token words stored after a page's records are
+ * not read: each record carries the scales of all its FP8 values.
+ *
+ * desc   head dims (576, 512), v_in_k = 1, num_kv_heads = 1, num_q_heads
+ *        1..16, kv_dtype SA_DTYPE_FP8_E4M3, kv_row_stride = 656; topk,
+ *        sm_scale and the q, idx, out row strides as for prefill
+ * pages  dst_page_tokens (a power of two), row_bytes = 656, scale_bytes,
+ *        dst_page_stride (>= dst_page_tokens * (row_bytes + scale_bytes), a
+ *        multiple of 16, < 2^32); the source fields are not used
+ * pool   device uint8, num_dst_pages pages at dst_page_stride, 16-byte
+ *        aligned; num_dst_pages * dst_page_tokens < 2^31
+ * topk_len  optional device int32 [batch], as for prefill
+ * ws     device workspace of sparse_attn_decode_workspace_bytes(batch,
+ *        num_q_heads, topk) bytes, 256-byte aligned, used only during the
+ *        call: each request's slots are cut into ranges of whole 16-slot
+ *        tiles, one workgroup per (request, range) writes that range's
+ *        normalised O and LSE there, and a second kernel merges them
+ * out    [batch][num_q_heads][512] fp32, lse [batch][num_q_heads] fp32,
+ *        fully written (a request with no valid slot gets O = 0, LSE = -inf)
+ */
+sa_status sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_page_desc* pages,
+                                   const void* q, const uint8_t* pool, int32_t num_dst_pages,
+                                   const int32_t* idx, const int32_t* topk_len, int32_t batch,
+                                   void* ws, size_t ws_bytes, float* out, float* lse,
+                                   hipStream_t stream);
+
 /* Host-only check of an attention descriptor, as sparse_attn_prefill (G=1)
  * or sparse_attn_prefill_union (G>1) would do before launching. Touches no
  * device. Returns SA_OK, SA_OK_FALLBACK (union tile illegal) or an error. */
@@ -274,7 +316,8 @@ typedef enum {
   SA_ENTRY_PAGE_MARK = 4,
   SA_ENTRY_PAGE_SPLIT = 5,
   SA_ENTRY_CHUNK_PREFILL_UNION = 6,
-  SA_ENTRY_COUNT = 7
+  SA_ENTRY_DECODE_PAGED = 7,
+  SA_ENTRY_COUNT = 8
 } sa_entry;
 uint64_t sa_call_count(int32_t entry);
 

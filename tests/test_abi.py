@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("sparse_attn_prefill", "sparse_attn_chunk_prefill", "sparse_attn_prefill_union",
                  "sparse_attn_union_build", "sparse_attn_union_workspace_bytes", "page_mark",
-                 "page_split", "sa_validate_attn", "sa_last_error", "sa_call_count"):
+                 "page_split", "sparse_attn_decode_paged", "sparse_attn_decode_workspace_bytes",
+                 "sa_validate_attn", "sa_last_error", "sa_call_count"):
         assert want in names
 
 
@@ -221,3 +222,52 @@ def test_fp8_records_validation():
     assert sa.sa_validate_attn(_mla(kv_dtype=sa.SA_DTYPE_FP8_E4M3, kv_row_stride=648)) == -2
     assert sa.sa_validate_attn(_mla(kv_dtype=sa.SA_DTYPE_FP8_E4M3, kv_row_stride=664)) == -2
     assert sa.sa_validate_attn(_mla(kv_dtype=7)) == -3
+
+
+def test_decode_workspace_bytes():
+    # ~512 (request, range) teams of whole 16-slot tiles: batch 32 x 2048
+    # slots -> 16 ranges of 128; partial O [512][8][512] fp32, then LSE
+    assert sa.sparse_attn_decode_workspace_bytes(32, 8, 2048) == 32 * 16 * 8 * 512 * 4 + 32 * 16 * 8 * 4
+    # batch 1: one range per tile (128 ranges)
+    assert sa.sparse_attn_decode_workspace_bytes(1, 8, 2048) == 128 * 8 * 2048 + 4096
+    # ragged tail: 100 slots at batch 512 -> one range of 112
+    assert sa.sparse_attn_decode_workspace_bytes(512, 2, 100) == 512 * 2 * 2048 + 4096
+    assert sa.sparse_attn_decode_workspace_bytes(0, 8, 2048) == 0
+    assert sa.sparse_attn_decode_workspace_bytes(4, 17, 2048) == 0
+    assert sa.sparse_attn_decode_workspace_bytes(4, 8, 0) == 0
+
+
+def test_decode_rejects_on_host():
+    lib = sa.lib()
+    f = lib.sparse_attn_decode_paged
+
+    def pg(**kw):
+        g = dict(src_page_tokens=256, dst_page_tokens=64, row_bytes=656, scale_bytes=4,
+                 src_page_stride=256 * 660, dst_page_stride=64 * 660)
+        g.update(kw)
+        return sa.PageDesc(**g)
+
+    fp8 = _mla(kv_dtype=sa.SA_DTYPE_FP8_E4M3, kv_row_stride=656)
+    ws = sa.sparse_attn_decode_workspace_bytes(32, 8, 2048)
+
+    def call(d=fp8, p=pg(), batch=32, w=0x10000, wb=ws, pool=0x2000):
+        return f(ctypes.byref(d), None if p is None else ctypes.byref(p), 0x1000, pool, 16384,
+                 0x3000, None, batch, w, wb, 0x4000, 0x5000, None)
+
+    assert call(d=_mla()) == -3                                     # bf16 rows
+    assert call(d=_mla(kv_dtype=sa.SA_DTYPE_FP8_E4M3, kv_row_stride=656, num_kv_heads=2,
+                       q_row_stride=8 * 576)) == -2                 # two latent heads
+    assert call(p=None) == -1
+    assert call(p=pg(dst_page_tokens=48)) == -2                     # not a power of two
+    assert call(p=pg(row_bytes=660)) == -2
+    assert call(d=_mla(kv_dtype=sa.SA_DTYPE_FP8_E4M3, kv_row_stride=672)) == -2
+    assert call(p=pg(dst_page_stride=64 * 660 + 8)) == -2          # not a multiple of 16
+    assert call(p=pg(dst_page_stride=64 * 600)) == -2               # shorter than a page
+    assert call(pool=None) == -1
+    assert call(w=None, wb=0) == -5
+    assert call(wb=ws - 1) == -5
+    assert call(w=0x10010) == -5                                    # misaligned workspace
+    assert call(batch=-1) == -2
+    before = sa.sa_call_count("sparse_attn_decode_paged")
+    assert call(batch=0, w=None, wb=0) == 0                         # nothing to launch, counted
+    assert sa.sa_call_count("sparse_attn_decode_paged") == before + 1

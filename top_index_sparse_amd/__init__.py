@@ -28,6 +28,8 @@ __all__ = [
     "sparse_attn_chunk_prefill_union",
     "page_mark",
     "page_split",
+    "sparse_attn_decode_workspace_bytes",
+    "sparse_attn_decode_paged",
     "sa_validate_attn",
     "sa_last_error",
     "sa_call_count",
@@ -48,7 +50,8 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_OK_FALLBACK", -1: "SA_ERR_NULL", -2: "SA_ERR_
                 -6: "SA_ERR_HIP"}
 ENTRIES = {"sparse_attn_prefill": 0, "sparse_attn_chunk_prefill": 1,
            "sparse_attn_union_build": 2, "sparse_attn_prefill_union": 3,
-           "page_mark": 4, "page_split": 5, "sparse_attn_chunk_prefill_union": 6}
+           "page_mark": 4, "page_split": 5, "sparse_attn_chunk_prefill_union": 6,
+           "sparse_attn_decode_paged": 7}
 
 
 class SparseAttnError(RuntimeError):
@@ -103,6 +106,9 @@ _SIGNATURES = {
                                                _I32, _I32, _I32, _P, _SZ, _P, _P, _P]),
     "page_mark": (_I32, [_P, _I64, _I32, _I32, _P, _P]),
     "page_split": (_I32, [ctypes.POINTER(PageDesc), _P, _P, _P, _I32, _P]),
+    "sparse_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "sparse_attn_decode_paged": (_I32, [ctypes.POINTER(AttnDesc), ctypes.POINTER(PageDesc), _P, _P,
+                                        _I32, _P, _P, _I32, _P, _SZ, _P, _P, _P]),
     "sa_validate_attn": (ctypes.c_int, [ctypes.POINTER(AttnDesc), _I32]),
     "sa_last_error": (ctypes.c_char_p, []),
     "sa_call_count": (ctypes.c_uint64, [_I32]),
@@ -430,3 +436,64 @@ def page_split(src: torch.Tensor, dst: torch.Tensor, mask: Optional[torch.Tensor
                           _stream(stream))
     _check(st, "page_split")
     return dst
+
+
+def sparse_attn_decode_workspace_bytes(batch: int, num_q_heads: int, topk: int) -> int:
+    return int(lib().sparse_attn_decode_workspace_bytes(batch, num_q_heads, topk))
+
+
+def sparse_attn_decode_paged(q: torch.Tensor, pool: torch.Tensor, idx: torch.Tensor, *,
+                             dst_page_tokens: int = 64, scale_bytes: int = 4,
+                             sm_scale: Optional[float] = None,
+                             topk_len: Optional[torch.Tensor] = None,
+                             ws: Optional[torch.Tensor] = None,
+                             out: Optional[torch.Tensor] = None,
+                             lse: Optional[torch.Tensor] = None,
+                             stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Sparse MLA decode over the split pool (C: sparse_attn_decode_paged).
+
+    q [B, Hq, 576] bf16 (one query row per request); pool uint8
+    [num_dst_pages, dst_page_stride] (pages of dst_page_tokens 656-byte FP8
+    records, then their per-token words); idx [B, topk] int32 pool token ids;
+    topk_len optional [B] int32. Returns (out [B, Hq, 512] fp32, lse [B, Hq]).
+    """
+    _need(q, "q", torch.bfloat16, 3)
+    _need(pool, "pool", torch.uint8, 2, q.device)
+    _need(idx, "idx", torch.int32, 2, q.device)
+    _rows_dense(q, "q")
+    _rows_dense(pool, "pool")
+    _rows_dense(idx, "idx")
+    B, Hq = q.shape[0], q.shape[1]
+    if idx.shape[0] != B:
+        raise ValueError(f"idx rows {idx.shape[0]} != batch {B}")
+    if topk_len is not None:
+        _need(topk_len, "topk_len", torch.int32, 1, q.device)
+        if topk_len.shape[0] != B or not topk_len.is_contiguous():
+            raise ValueError("topk_len must be a contiguous [B] tensor")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[2])
+    if out is None:
+        out = torch.empty((B, Hq, 512), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 3, q.device)
+    _need(lse, "lse", torch.float32, 2, q.device)
+    _rows_dense(out, "out")
+    if not lse.is_contiguous():
+        raise ValueError("lse must be contiguous")
+    desc = AttnDesc(num_q_heads=Hq, num_kv_heads=1, head_dim_qk=q.shape[2], head_dim_v=512,
+                    topk=idx.shape[1], v_in_k=1, kv_dtype=SA_DTYPE_FP8_E4M3,
+                    sm_scale=float(sm_scale), q_row_stride=q.stride(0),
+                    kv_row_stride=FP8_RECORD_BYTES, v_row_stride=FP8_RECORD_BYTES,
+                    idx_row_stride=idx.stride(0), out_row_stride=out.stride(0))
+    pages = PageDesc(src_page_tokens=0, dst_page_tokens=dst_page_tokens,
+                     row_bytes=FP8_RECORD_BYTES, scale_bytes=scale_bytes, src_page_stride=0,
+                     dst_page_stride=pool.stride(0))
+    nbytes = sparse_attn_decode_workspace_bytes(B, Hq, idx.shape[1])
+    ws = _workspace(ws, nbytes, q.device) if B > 0 else ws
+    st = lib().sparse_attn_decode_paged(ctypes.byref(desc), ctypes.byref(pages), _ptr(q),
+                                        _ptr(pool), pool.shape[0], _ptr(idx), _ptr(topk_len), B,
+                                        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                        _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "sparse_attn_decode_paged")
+    return out, lse

@@ -203,6 +203,32 @@ bool chunk_union_layout(int32_t total_q, int32_t num_reqs, int32_t topk, int32_t
   return true;
 }
 
+// Slot ranges of a decode launch: about kDecodeTeams (request, range) teams
+// over the batch (two per CU), each range whole 16-slot tiles. Workspace:
+// normalised partial O [batch * splits][heads][512] fp32, then partial LSE
+// [batch * splits][heads] fp32, each 256-byte aligned.
+constexpr int64_t kDecodeTeams = 512;
+
+struct DecodeLayout {
+  int32_t splits, split_len;
+  int64_t lse_off, total;
+};
+
+bool decode_layout(int32_t batch, int32_t num_q_heads, int32_t topk, DecodeLayout* L) {
+  if (batch < 0 || num_q_heads <= 0 || num_q_heads > 16 || topk <= 0) return false;
+  const int64_t tiles = ((int64_t)topk + 15) / 16;
+  int64_t s = batch > 0 ? (kDecodeTeams + batch - 1) / batch : 1;
+  if (s > tiles) s = tiles;
+  const int64_t len = (tiles + s - 1) / s * 16;
+  L->split_len = (int32_t)len;
+  L->splits = (int32_t)(((int64_t)topk + len - 1) / len);
+  const int64_t rows = (int64_t)batch * L->splits;
+  if (rows > INT32_MAX) return false;
+  L->lse_off = align_up(rows * num_q_heads * 512 * 4, 256);
+  L->total = L->lse_off + align_up(rows * num_q_heads * 4, 256);
+  return true;
+}
+
 sa::UnionBuildParams build_params(const int32_t* idx, int64_t idx_row_stride, int32_t num_rows,
                                   int32_t topk, int32_t kv_len, int32_t G, const UnionLayout& L,
                                   void* ws) {
@@ -434,6 +460,83 @@ sa_status sparse_attn_chunk_prefill_union(const sa_attn_desc* desc, const void* 
   p.gstart = gstart;
   st = launch_attention(kernel, p, 1, stream);
   return st == SA_OK ? ok(SA_ENTRY_CHUNK_PREFILL_UNION) : st;
+}
+
+size_t sparse_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t topk) {
+  DecodeLayout L;
+  if (!decode_layout(batch, num_q_heads, topk, &L)) return 0;
+  return (size_t)L.total;
+}
+
+sa_status sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_page_desc* pages,
+                                   const void* q, const uint8_t* pool, int32_t num_dst_pages,
+                                   const int32_t* idx, const int32_t* topk_len, int32_t batch,
+                                   void* ws, size_t ws_bytes, float* out, float* lse,
+                                   hipStream_t stream) {
+  g_err[0] = 0;
+  Kernel kernel = Kernel::kNone;
+  sa_status st = check_desc(desc, 1, &kernel);
+  if (st != SA_OK) return st;
+  if (kernel != Kernel::kMla576Fp8)
+    return fail(SA_ERR_DTYPE, "decode reads FP8 MLA records: head dims (576, 512), v_in_k, "
+                              "kv_dtype SA_DTYPE_FP8_E4M3");
+  if (desc->num_kv_heads != 1)
+    return fail(SA_ERR_SHAPE, "a page row holds one latent record per token: num_kv_heads %d != 1",
+                desc->num_kv_heads);
+  if (!pages) return fail(SA_ERR_NULL, "pages is NULL");
+  const int32_t ptok = pages->dst_page_tokens;
+  if (ptok <= 0 || (ptok & (ptok - 1)) || ptok > (1 << 20))
+    return fail(SA_ERR_SHAPE, "dst_page_tokens %d must be a power of two <= 2^20", ptok);
+  if (pages->row_bytes != kFp8RecordBytes || desc->kv_row_stride != kFp8RecordBytes)
+    return fail(SA_ERR_SHAPE, "token rows are 656-byte records: row_bytes %d, kv_row_stride %lld",
+                pages->row_bytes, (long long)desc->kv_row_stride);
+  if (pages->scale_bytes < 0) return fail(SA_ERR_SHAPE, "scale_bytes %d < 0", pages->scale_bytes);
+  const int64_t page_min = (int64_t)ptok * (pages->row_bytes + pages->scale_bytes);
+  if (pages->dst_page_stride < page_min || pages->dst_page_stride % 16 ||
+      pages->dst_page_stride >= (int64_t)1 << 32)
+    return fail(SA_ERR_SHAPE, "dst_page_stride %lld: needs >= %lld, a multiple of 16, < 2^32",
+                (long long)pages->dst_page_stride, (long long)page_min);
+  if (num_dst_pages < 0 || batch < 0)
+    return fail(SA_ERR_SHAPE, "num_dst_pages %d and batch %d must be >= 0", num_dst_pages, batch);
+  if ((int64_t)num_dst_pages * ptok > INT32_MAX)
+    return fail(SA_ERR_SHAPE, "pool tokens (%d pages x %d) must stay below 2^31", num_dst_pages,
+                ptok);
+  DecodeLayout L;
+  if (!decode_layout(batch, desc->num_q_heads, desc->topk, &L))
+    return fail(SA_ERR_SHAPE, "decode of batch %d x topk %d does not fit one launch", batch,
+                desc->topk);
+  if (batch == 0) return ok(SA_ENTRY_DECODE_PAGED);
+  st = check_ptrs(desc, q, pool, nullptr, idx, out, lse);
+  if (st != SA_OK) return st;
+  if (!ws || ws_bytes < (size_t)L.total || (reinterpret_cast<uintptr_t>(ws) & 255u))
+    return fail(SA_ERR_WORKSPACE, "ws: needs %lld bytes, 256-byte aligned (got %zu)",
+                (long long)L.total, ws_bytes);
+  float* part_out = static_cast<float*>(ws);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + L.lse_off);
+  const int32_t rows = batch * L.splits;
+  sa::AttnParams p = make_params(desc, q, pool, nullptr, idx, part_out, part_lse, rows);
+  p.out_row_stride = (int64_t)desc->num_q_heads * 512;
+  p.topk_len = topk_len;
+  p.kv_len = num_dst_pages * ptok;
+  p.num_reqs = 1;
+  p.dec_splits = L.splits;
+  p.dec_split_len = L.split_len;
+  int shift = 0;
+  while ((1 << shift) < ptok) ++shift;
+  p.page_shift = shift;
+  p.page_stride = pages->dst_page_stride;
+  sa::DecodeCombineParams c{};
+  c.part_out = part_out;
+  c.part_lse = part_lse;
+  c.out = out;
+  c.lse = lse;
+  c.out_row_stride = desc->out_row_stride;
+  c.batch = batch;
+  c.splits = L.splits;
+  c.num_q_heads = desc->num_q_heads;
+  const hipError_t e = sa::launch_decode_mla576_fp8(p, c, stream);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok(SA_ENTRY_DECODE_PAGED);
 }
 
 sa_status page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src_pages,

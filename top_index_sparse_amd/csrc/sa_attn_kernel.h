@@ -71,7 +71,9 @@ namespace sa {
 
 // kRows: per-token results (one request, or ragged requests when cu_q is
 // set), rows grouped into teams by position. kUnion: prebuilt union lists.
-enum : int { kRows = 0, kUnion = 1 };
+// kDecode: one team per (request, slot range) over paged FP8 records, each
+// writing that range's normalised result for a later merge.
+enum : int { kRows = 0, kUnion = 1, kDecode = 2 };
 
 // Headroom of the running max in log2 units: probabilities stay <= 2^kSlack.
 constexpr float kSlack = 8.f;
@@ -101,6 +103,7 @@ struct AttnTile {
   // FP8: K rows are 656-byte records (512 E4M3 latent values, four fp32
   // block scales, 64 bf16 rope values), dequantised into the same bf16 slice
   static_assert(!FP8 || (VKLDS && DQK == 576 && DV == 512 && WSPLIT == 2), "FP8 records");
+  static_assert(MODE != kDecode || (FP8 && C == 1), "decode reads paged FP8 records, one row per team");
   static constexpr int KCH = KLDS ? KSTEPS / 4 : 0;   // 16-byte K chunks per slot per lane
   static constexpr int KROW = 64 * KSTEPS + 16;       // LDS row pitch (bytes): 16 (mod 32) * odd
   static constexpr int KLDS_BYTES = 16 * KROW;
@@ -124,6 +127,7 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   constexpr int VCH = TT::VCH;
   constexpr int MTILES = TT::MTILES;
   constexpr bool UNION = TT::UNION;
+  constexpr bool DECODE = MODE == kDecode;
   constexpr bool VKLDS = TT::VKLDS;
   constexpr int KCH = TT::KCH;
   constexpr int KROW = TT::KROW;
@@ -151,7 +155,8 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   int base_l = 0;             // per-token: first KV row of this lane's request
   int len_l = 0;              // and its length
   int64_t team_kv = 0;        // union over ragged requests: the group's first KV row
-  if (UNION) {
+  int qrow_div = 1;           // decode: a virtual row's query row is row / dec_splits
+  if constexpr (UNION) {
     const int per_head = p.num_groups * p.teams_per_group;
     kvh = team_id / per_head;
     if (kvh >= p.num_kv_heads) return;
@@ -177,6 +182,30 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     irow = p.union_idx + (int64_t)gi * p.union_stride;
     brow = p.union_bits + (int64_t)gi * p.union_stride;
     jmax = p.union_len[gi];
+  } else if constexpr (DECODE) {
+    // virtual row t0 = b * dec_splits + s: slots [s L, s L + L) of request b
+    kvh = team_id / p.num_rows;
+    if (kvh >= p.num_kv_heads) return;
+    t0 = team_id - kvh * p.num_rows;
+    rows = 1;
+    qrow_div = p.dec_splits;
+    const int b = t0 / p.dec_splits;
+    const int j0 = (t0 - b * p.dec_splits) * p.dec_split_len;
+    if (row_l == 0) {
+      len_l = p.kv_len;   // tokens in the pool
+      int lim = p.topk;
+      if (p.topk_len) {
+        const int tl = p.topk_len[b];
+        lim = tl < 0 ? 0 : (tl < lim ? tl : lim);
+      }
+      jmax_l = lim - j0;
+      jmax_l = jmax_l < 0 ? 0 : (jmax_l < p.dec_split_len ? jmax_l : p.dec_split_len);
+    }
+    irow = p.idx + (int64_t)b * p.idx_row_stride + j0;
+    int jm = jmax_l;
+    jm = max(jm, __builtin_amdgcn_mov_dpp(jm, 0xb1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+    jm = max(jm, __builtin_amdgcn_mov_dpp(jm, 0x4e, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+    jmax = __builtin_amdgcn_readfirstlane(jm);
   } else {
     const int per_head = (p.num_rows + p.rows_per_team - 1) / p.rows_per_team;
     kvh = team_id / per_head;
@@ -236,7 +265,7 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     bool live;
     int t, head;
     col_bit[c] = column(c, live, t, head);
-    const uint16_t* qp = p.q + (int64_t)t * p.q_row_stride + (int64_t)head * DQK + 8 * g;
+    const uint16_t* qp = p.q + (int64_t)(t / qrow_div) * p.q_row_stride + (int64_t)head * DQK + 8 * g;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       // d of k-step s: the wave's slice in k-step order
@@ -313,7 +342,13 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   // when slot 4g+i contributes to column n of tile c.
   auto load_data = [&](Data& td, const Tile& tl, uint32_t mask[C]) {
     const bool ok = tl.tok >= 0 && (tl.bits & team_bits);
-    const int64_t koff = ok ? (int64_t)((uint64_t)(uint32_t)tl.tok * k_row_bytes) : -1;
+    int64_t koff;
+    if constexpr (DECODE)   // record (t & mask) of page t >> shift (page stride < 2^32)
+      koff = ok ? (int64_t)((uint64_t)((uint32_t)tl.tok >> p.page_shift) * (uint32_t)p.page_stride +
+                            ((uint32_t)tl.tok & ((1u << p.page_shift) - 1u)) * 656u)
+                : -1;
+    else
+      koff = ok ? (int64_t)((uint64_t)(uint32_t)tl.tok * k_row_bytes) : -1;
     int khi[4], bq[4];
     row_bcast4((int)(koff >> 32), khi);
     row_bcast4((int)tl.bits, bq);
@@ -564,7 +599,9 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     bool live;
     int t, head;
     column(c, live, t, head);
-    if (live) {
+    // decode: a range with no valid slot leaves its O unwritten (the merge
+    // gives it weight 0 from its LSE)
+    if (live && (!DECODE || l > 0.f)) {
       const float inv = l > 0.f ? 1.f / l : 0.f;
       float* orow = p.out + (int64_t)t * p.out_row_stride + (int64_t)head * DV;
 #pragma unroll
@@ -580,10 +617,10 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
           st16(orow + d0 + 4, hi * inv);
         }
       }
-      if (g == 0 && split == 0)
-        p.lse[(int64_t)t * p.num_q_heads + head] =
-            l > 0.f ? (m_run[c] + fast_log2(l)) * kLn2 : -INFINITY;
     }
+    if (live && g == 0 && split == 0)
+      p.lse[(int64_t)t * p.num_q_heads + head] =
+          l > 0.f ? (m_run[c] + fast_log2(l)) * kLn2 : -INFINITY;
   }
 }
 

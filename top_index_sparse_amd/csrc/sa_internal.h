@@ -41,6 +41,26 @@ struct AttnParams {
   int32_t teams_per_group;    // union: teams serving one group
   // rows one team serves (per-token: consecutive rows; union: group members)
   int32_t rows_per_team;
+  // decode over pages: virtual row b * dec_splits + s covers slots
+  // [s * dec_split_len, (s + 1) * dec_split_len) of request b; token t is
+  // the record at byte (t >> page_shift) * page_stride + (t & mask) * 656
+  int32_t dec_splits;
+  int32_t dec_split_len;
+  int32_t page_shift;
+  int64_t page_stride;
+};
+
+// Merge of the per-range decode results: out[b, h] and lse[b, h] from
+// part_out[b * splits + s, h] and part_lse[b * splits + s, h].
+struct DecodeCombineParams {
+  const float* part_out;      // [batch * splits][num_q_heads][512], normalised
+  const float* part_lse;      // [batch * splits][num_q_heads], natural log
+  float* out;
+  float* lse;
+  int64_t out_row_stride;
+  int32_t batch;
+  int32_t splits;
+  int32_t num_q_heads;
 };
 
 struct UnionBuildParams {
@@ -105,6 +125,10 @@ struct PageParams {
 hipError_t launch_attn_gqa256(AttnParams p, int union_mode, hipStream_t stream);
 hipError_t launch_attn_mla576(AttnParams p, int union_mode, hipStream_t stream);
 hipError_t launch_attn_mla576_fp8(AttnParams p, int union_mode, hipStream_t stream);
+// Decode over 64-token pages of FP8 records: the per-range team kernel
+// (p.out / p.lse point at the partials), then the combine.
+hipError_t launch_decode_mla576_fp8(AttnParams p, const DecodeCombineParams& c,
+                                    hipStream_t stream);
 hipError_t launch_union_build(const UnionBuildParams& p, hipStream_t stream);
 // Ragged: writes gstart[0..num_reqs] from cu_q, then builds every group's
 // union over its request's KV range with bit planes.
