@@ -40,6 +40,7 @@ import gen  # noqa: E402
 
 METRIC = "sparse prefill ms/call + gathered-KV GB/s (% HBM roofline), 8192 rows × 2051 slots"
 HBM_PEAK_GBS = 8000.0
+FP8_RECORD_BYTES = 656          # one FP8 MLA record per gathered decode slot
 KERNEL_SOURCE = os.path.join(ROOT, "top_index_sparse_amd", "csrc", "sa_gqa.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gqa_d256_c1_traffic.txt")
 
@@ -303,6 +304,46 @@ def measure_others(args, sa, torch, stream):
         "full_GBps": round(2 * c.num_src_pages * page_bytes / (ms_full * 1e-3) / 1e9, 1),
         "full_frac_hbm_peak": round(2 * c.num_src_pages * page_bytes / (ms_full * 1e-3) / 1e9
                                     / HBM_PEAK_GBS, 4)}
+
+    # sparse MLA decode over the split pages, and the whole decode step
+    # (mark + masked split + decode); then the spread indices (2048 valid
+    # slots per request, 1947 touched pages)
+    def decode_lines(c, src, dst, didx, mask):
+        geom = dict(src_page_tokens=c.src_page_tokens, dst_page_tokens=c.dst_page_tokens,
+                    row_bytes=c.row_bytes, scale_bytes=c.scale_bytes, stream=stream)
+        B, Hq, topk = c.q.shape[0], c.q.shape[1], c.idx.shape[1]
+        dq = torch.from_numpy(c.q.view(np.int16)).view(torch.bfloat16).cuda()
+        dws = torch.empty(sa.sparse_attn_decode_workspace_bytes(B, Hq, topk), dtype=torch.uint8,
+                          device="cuda")
+        dout = torch.empty((B, Hq, 512), dtype=torch.float32, device="cuda")
+        dlse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+
+        def decode():
+            sa.sparse_attn_decode_paged(dq, dst, didx, dst_page_tokens=c.dst_page_tokens,
+                                        scale_bytes=c.scale_bytes, sm_scale=c.scale, ws=dws,
+                                        out=dout, lse=dlse, stream=stream)
+
+        def step():
+            sa.page_mark(didx, c.num_src_pages, c.src_page_tokens, mask=mask, stream=stream)
+            sa.page_split(src, dst, mask, **geom)
+            decode()
+
+        step()
+        ms_dec = _events_ms(torch, stream, decode, w, n)
+        ms_step = _events_ms(torch, stream, step, w, n)
+        valid = int(((c.idx >= 0) & (c.idx < c.num_src_pages * c.src_page_tokens)).sum())
+        r = _rate(valid * FP8_RECORD_BYTES, ms_dec)
+        r.update({"valid_slots": valid, "step_ms": round(ms_step, 4)})
+        return r
+
+    res["decode_attention"] = decode_lines(c, src, dst, didx, mask)
+    del src, dst
+    c = gen.make_config("C4spread", args.seed)
+    src = torch.from_numpy(c.src).cuda()
+    dst = torch.full((c.num_src_pages * c.ratio, c.dst_page_bytes), 0xA5, dtype=torch.uint8,
+                     device="cuda")
+    didx = torch.from_numpy(c.idx).cuda()
+    res["decode_attention_spread"] = decode_lines(c, src, dst, didx, mask)
     return res
 
 

@@ -286,8 +286,8 @@ size_t sparse_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, in
  * topk_len  optional device int32 [batch], as for prefill
  * ws     device workspace of sparse_attn_decode_workspace_bytes(batch,
  *        num_q_heads, topk) bytes, 256-byte aligned, used only during the
- *        call: each request's slots are cut into ranges of whole 16-slot
- *        tiles, one workgroup per (request, range) writes that range's
+ *        call: each request's 16-slot tiles are dealt round-robin to S
+ *        ranges, one workgroup per (request, range) writes that range's
  *        normalised O and LSE there, and a second kernel merges them
  * out    [batch][num_q_heads][512] fp32, lse [batch][num_q_heads] fp32,
  *        fully written (a request with no valid slot gets O = 0, LSE = -inf)

@@ -203,14 +203,18 @@ bool chunk_union_layout(int32_t total_q, int32_t num_reqs, int32_t topk, int32_t
   return true;
 }
 
-// Slot ranges of a decode launch: about kDecodeTeams (request, range) teams
-// over the batch (two per CU), each range whole 16-slot tiles. Workspace:
-// normalised partial O [batch * splits][heads][512] fp32, then partial LSE
-// [batch * splits][heads] fp32, each 256-byte aligned.
-constexpr int64_t kDecodeTeams = 512;
+// Slot ranges of a decode launch. Range s of S takes a request's 16-slot
+// tiles s, s + S, s + 2S, ... (so a request whose valid slots come first
+// still spreads them over its ranges). S aims at kDecodeTeams (request,
+// range) teams, as many as the chip holds at once, and at most
+// kDecodeTilesPerRange tiles per range. Workspace: normalised partial O
+// [batch * S][heads][512] fp32, then partial LSE [batch * S][heads] fp32,
+// each 256-byte aligned.
+constexpr int64_t kDecodeTeams = 1024;
+constexpr int64_t kDecodeTilesPerRange = 8;
 
 struct DecodeLayout {
-  int32_t splits, split_len;
+  int32_t splits;
   int64_t lse_off, total;
 };
 
@@ -218,10 +222,10 @@ bool decode_layout(int32_t batch, int32_t num_q_heads, int32_t topk, DecodeLayou
   if (batch < 0 || num_q_heads <= 0 || num_q_heads > 16 || topk <= 0) return false;
   const int64_t tiles = ((int64_t)topk + 15) / 16;
   int64_t s = batch > 0 ? (kDecodeTeams + batch - 1) / batch : 1;
+  const int64_t s_min = (tiles + kDecodeTilesPerRange - 1) / kDecodeTilesPerRange;
+  if (s < s_min) s = s_min;
   if (s > tiles) s = tiles;
-  const int64_t len = (tiles + s - 1) / s * 16;
-  L->split_len = (int32_t)len;
-  L->splits = (int32_t)(((int64_t)topk + len - 1) / len);
+  L->splits = (int32_t)s;
   const int64_t rows = (int64_t)batch * L->splits;
   if (rows > INT32_MAX) return false;
   L->lse_off = align_up(rows * num_q_heads * 512 * 4, 256);
@@ -520,7 +524,6 @@ sa_status sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_page_desc*
   p.kv_len = num_dst_pages * ptok;
   p.num_reqs = 1;
   p.dec_splits = L.splits;
-  p.dec_split_len = L.split_len;
   int shift = 0;
   while ((1 << shift) < ptok) ++shift;
   p.page_shift = shift;

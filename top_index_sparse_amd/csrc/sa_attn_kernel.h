@@ -72,7 +72,8 @@ namespace sa {
 // kRows: per-token results (one request, or ragged requests when cu_q is
 // set), rows grouped into teams by position. kUnion: prebuilt union lists.
 // kDecode: one team per (request, slot range) over paged FP8 records, each
-// writing that range's normalised result for a later merge.
+// writing that range's normalised result for a later merge; range s of S
+// takes the request's slot tiles s, s + S, s + 2S, ...
 enum : int { kRows = 0, kUnion = 1, kDecode = 2 };
 
 // Headroom of the running max in log2 units: probabilities stay <= 2^kSlack.
@@ -156,6 +157,8 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   int len_l = 0;              // and its length
   int64_t team_kv = 0;        // union over ragged requests: the group's first KV row
   int qrow_div = 1;           // decode: a virtual row's query row is row / dec_splits
+  int tile_first = 0;         // decode: the range's first slot tile and tile stride
+  int tile_step = 1;
   if constexpr (UNION) {
     const int per_head = p.num_groups * p.teams_per_group;
     kvh = team_id / per_head;
@@ -183,25 +186,24 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     brow = p.union_bits + (int64_t)gi * p.union_stride;
     jmax = p.union_len[gi];
   } else if constexpr (DECODE) {
-    // virtual row t0 = b * dec_splits + s: slots [s L, s L + L) of request b
+    // virtual row t0 = b * dec_splits + s: slot tiles s, s + S, ... of request b
     kvh = team_id / p.num_rows;
     if (kvh >= p.num_kv_heads) return;
     t0 = team_id - kvh * p.num_rows;
     rows = 1;
     qrow_div = p.dec_splits;
     const int b = t0 / p.dec_splits;
-    const int j0 = (t0 - b * p.dec_splits) * p.dec_split_len;
+    tile_first = t0 - b * p.dec_splits;
+    tile_step = p.dec_splits;
     if (row_l == 0) {
       len_l = p.kv_len;   // tokens in the pool
-      int lim = p.topk;
+      jmax_l = p.topk;
       if (p.topk_len) {
         const int tl = p.topk_len[b];
-        lim = tl < 0 ? 0 : (tl < lim ? tl : lim);
+        jmax_l = tl < 0 ? 0 : (tl < jmax_l ? tl : jmax_l);
       }
-      jmax_l = lim - j0;
-      jmax_l = jmax_l < 0 ? 0 : (jmax_l < p.dec_split_len ? jmax_l : p.dec_split_len);
     }
-    irow = p.idx + (int64_t)b * p.idx_row_stride + j0;
+    irow = p.idx + (int64_t)b * p.idx_row_stride;
     int jm = jmax_l;
     jm = max(jm, __builtin_amdgcn_mov_dpp(jm, 0xb1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
     jm = max(jm, __builtin_amdgcn_mov_dpp(jm, 0x4e, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
@@ -241,7 +243,8 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     jmax = __builtin_amdgcn_readfirstlane(jm);
   }
   const uint32_t team_bits = ((1u << rows) - 1u) << bit0;
-  const int ntiles = (jmax + TILE - 1) / TILE;
+  const int tiles_all = (jmax + TILE - 1) / TILE;
+  const int ntiles = tiles_all > tile_first ? (tiles_all - tile_first + tile_step - 1) / tile_step : 0;
 
   // ---- columns: tile c, lane n -> row j, head ----------------------------
   // (recomputed in the epilogue so that only the ownership bits stay live)
@@ -565,13 +568,13 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   // Main tiles: the next tile's indices load while this one is gathered and
   // consumed (loads retire in issue order, so they are issued first).
   Idx ib[2];
-  if (ntiles > 0) load_idx(ib[0], 0);
+  if (ntiles > 0) load_idx(ib[0], tile_first * TILE);
   for (int tile = 0; tile < ntiles; tile += 2) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int cur = tile + u;
       if (cur >= ntiles) break;
-      if (cur + 1 < ntiles) load_idx(ib[u ^ 1], (cur + 1) * TILE);
+      if (cur + 1 < ntiles) load_idx(ib[u ^ 1], (tile_first + (cur + 1) * tile_step) * TILE);
       __builtin_amdgcn_sched_barrier(0);
       Tile tl;
       if constexpr (UNION) {
@@ -580,10 +583,17 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
       } else {
         tl = resolve(ib[u]);
       }
-      uint32_t mask[C];
-      load_data(db, tl, mask);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(db, mask);
+      // A tile with nothing to gather for this team is skipped: its scores
+      // would all be -inf, which leaves the softmax state and O unchanged.
+      // Every wave of the team sees the same tile, so all take the branch.
+      // (The three-tile shape keeps the straight path: the branch costs it
+      // more register spills than the tiles it could skip.)
+      if (C == 3 || __ballot(tl.tok >= 0 && (tl.bits & team_bits)) != 0) {
+        uint32_t mask[C];
+        load_data(db, tl, mask);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(db, mask);
+      }
       // per-token modes: queue tiles whenever 16 queued tokens wait (so the
       // queue never holds more than 63), and a last one for the rest
       if constexpr (!UNION) run_queue(false);
@@ -599,28 +609,30 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     bool live;
     int t, head;
     column(c, live, t, head);
-    // decode: a range with no valid slot leaves its O unwritten (the merge
-    // gives it weight 0 from its LSE)
-    if (live && (!DECODE || l > 0.f)) {
+    if (live) {
       const float inv = l > 0.f ? 1.f / l : 0.f;
       float* orow = p.out + (int64_t)t * p.out_row_stride + (int64_t)head * DV;
+      // decode: a range with no valid slot leaves its O unwritten (the merge
+      // gives it weight 0 from its LSE)
+      if (!DECODE || l > 0.f) {
 #pragma unroll
-      for (int h = 0; h < VCH; ++h) {
+        for (int h = 0; h < VCH; ++h) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d0 = 128 * (VCH * split + h) + 32 * g + 8 * i;
-          const f32x4_t lo = {acc[c][8 * h + 0][i], acc[c][8 * h + 1][i], acc[c][8 * h + 2][i],
-                              acc[c][8 * h + 3][i]};
-          const f32x4_t hi = {acc[c][8 * h + 4][i], acc[c][8 * h + 5][i], acc[c][8 * h + 6][i],
-                              acc[c][8 * h + 7][i]};
-          st16(orow + d0, lo * inv);
-          st16(orow + d0 + 4, hi * inv);
+          for (int i = 0; i < 4; ++i) {
+            const int d0 = 128 * (VCH * split + h) + 32 * g + 8 * i;
+            const f32x4_t lo = {acc[c][8 * h + 0][i], acc[c][8 * h + 1][i], acc[c][8 * h + 2][i],
+                                acc[c][8 * h + 3][i]};
+            const f32x4_t hi = {acc[c][8 * h + 4][i], acc[c][8 * h + 5][i], acc[c][8 * h + 6][i],
+                                acc[c][8 * h + 7][i]};
+            st16(orow + d0, lo * inv);
+            st16(orow + d0 + 4, hi * inv);
+          }
         }
       }
+      if (g == 0 && split == 0)
+        p.lse[(int64_t)t * p.num_q_heads + head] =
+            l > 0.f ? (m_run[c] + fast_log2(l)) * kLn2 : -INFINITY;
     }
-    if (live && g == 0 && split == 0)
-      p.lse[(int64_t)t * p.num_q_heads + head] =
-          l > 0.f ? (m_run[c] + fast_log2(l)) * kLn2 : -INFINITY;
   }
 }
 

@@ -41,11 +41,10 @@ struct AttnParams {
   int32_t teams_per_group;    // union: teams serving one group
   // rows one team serves (per-token: consecutive rows; union: group members)
   int32_t rows_per_team;
-  // decode over pages: virtual row b * dec_splits + s covers slots
-  // [s * dec_split_len, (s + 1) * dec_split_len) of request b; token t is
-  // the record at byte (t >> page_shift) * page_stride + (t & mask) * 656
+  // decode over pages: virtual row b * dec_splits + s covers slot tiles
+  // s, s + dec_splits, ... of request b; token t is the record at byte
+  // (t >> page_shift) * page_stride + (t & mask) * 656
   int32_t dec_splits;
-  int32_t dec_split_len;
   int32_t page_shift;
   int64_t page_stride;
 };
