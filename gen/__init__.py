@@ -381,8 +381,47 @@ def make_page_case(name: str, *, seed: int, num_src_pages: int = 4096,
     return PageCase(name, src, idx, src_page_tokens, dst_page_tokens, row_bytes, scale_bytes, q)
 
 
+@dataclasses.dataclass
+class TopkCase:
+    """Indexer scores of one chunk of query rows and the selection budget.
+
+    scores   float32 [T, kv_len]: row t's scores for positions 0 .. kv_len-1
+    row_len  int32 [T]: positions visible to row t (its position + 1)
+    """
+    name: str
+    scores: np.ndarray
+    row_len: np.ndarray
+    k: int
+
+    def arrays(self) -> Dict[str, np.ndarray]:
+        return {"scores": self.scores, "row_len": self.row_len}
+
+
+def drifting_scores(rng: np.random.Generator, T: int, kv: int, drift: float) -> np.ndarray:
+    """float32 [T, kv]: an N(0,1) base score per position plus, per
+    position, a random walk over the rows with N(0, drift^2) steps, so that
+    neighbouring rows rank positions almost alike."""
+    x = rng.standard_normal(kv, dtype=np.float32)
+    s = rng.standard_normal((T, kv), dtype=np.float32)
+    s *= np.float32(drift)
+    np.cumsum(s, axis=0, out=s)
+    s += x
+    return s
+
+
+def make_topk_case(name: str, *, seed: int, num_rows: int, kv_len: int, first_pos: int,
+                   k: int, drift: float = 0.027) -> TopkCase:
+    """Rows at positions first_pos .. first_pos+num_rows-1 of one request.
+    drift 0.027 changes about 2 % of a 2051-slot selection per row over
+    ~30k visible positions, the walk's rate."""
+    rng = _streams(seed)[3]
+    scores = drifting_scores(rng, num_rows, kv_len, drift)
+    row_len = np.arange(first_pos + 1, first_pos + num_rows + 1, dtype=np.int32)
+    return TopkCase(name, scores, row_len, k)
+
+
 CONFIG_NAMES = ("C0a", "C0b", "C1", "C2", "C3", "C3tail", "C3fp8", "C4", "C4decode",
-                "C4spread")
+                "C4spread", "C0topk", "C1topk")
 
 
 def make_config(name: str, seed: int = 0):
@@ -407,6 +446,10 @@ def make_config(name: str, seed: int = 0):
          batch 32 x 2048 indices over each request's last 256 tokens (the
          referenced rows are FP8 MLA records), 8 MLA query heads per request
     C4spread  the same pool with 2048 indices spread over each context
+    C0topk  indexer scores for 128 rows at positions 0..127 over 512
+         positions, top-k 64 (rows t < 63 select everything and pad)
+    C1topk  indexer scores for C1's 8192 rows (positions 24576..32767) over
+         32768 positions, top-k 2051
     """
     if name == "C0a":
         return make_attn_case(name, seed=seed, num_rows=128, kv_len=512, first_pos=0,
@@ -444,6 +487,11 @@ def make_config(name: str, seed: int = 0):
         return make_page_case(name, seed=seed)
     if name == "C4spread":
         return make_page_case(name, seed=seed, spread=True)
+    if name == "C0topk":
+        return make_topk_case(name, seed=seed, num_rows=128, kv_len=512, first_pos=0, k=64)
+    if name == "C1topk":
+        return make_topk_case(name, seed=seed, num_rows=8192, kv_len=32768,
+                              first_pos=32768 - 8192, k=2051)
     raise KeyError(f"unknown config {name!r}; known: {CONFIG_NAMES}")
 
 

@@ -14,6 +14,7 @@ union       union-of-G index build (sorted, deduplicated, ownership bits) and
 pages       decode-pool page mark and (masked) page split
 fp8         the 656-byte FP8 MLA record and its dequantisation to bf16
 decode      sparse MLA decode over the split pages of FP8 records
+topk        the indexer's top-k selection from scores to index rows
 
 Every function cites the passage of the pages it restates. Where the pages
 leave a point open, the reading taken is stated at the function.
@@ -28,6 +29,7 @@ from .union import union_build, union_attention, chunk_union_build, chunk_union_
 from .pages import page_mark, page_split
 from .fp8 import fp8_e4m3_to_f64, mla_fp8_rows_to_f64
 from .decode import paged_decode, paged_record
+from .topk import topk_select
 
 __all__ = [
     "bf16_to_f64",
@@ -43,6 +45,7 @@ __all__ = [
     "mla_fp8_rows_to_f64",
     "paged_decode",
     "paged_record",
+    "topk_select",
     "page_mark",
     "page_split",
 ]

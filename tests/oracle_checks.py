@@ -512,3 +512,66 @@ def check_paged_decode_vs_source(paged_decode, sparse_attention, mla_fp8_rows_to
         fin = np.isfinite(want_l)
         assert np.array_equal(fin, np.isfinite(got_l)), "empty rows"
         assert np.allclose(got_l[fin], want_l[fin], rtol=0, atol=1e-12), "decode LSE"
+
+
+# --------------------------------------------------------------------------
+# indexer top-k selection
+
+def _rank_count_select(row, n, k):
+    """Brute force: position j < n is selected iff fewer than k positions
+    beat it (a larger score, or an equal score at a lower position)."""
+    sel = []
+    for j in range(n):
+        beat = sum(1 for i in range(n) if row[i] > row[j] or (row[i] == row[j] and i < j))
+        if beat < k:
+            sel.append(j)
+    return sel + [-1] * (k - len(sel))
+
+
+def check_topk_rank_count(topk_select, seed=31):
+    """Small rows with many ties, signed zeros and infinities, lengths from
+    0 to past the row, against the rank-count characterisation."""
+    rng = np.random.default_rng(seed)
+    T, kv = 7, 40
+    s = np.round(rng.standard_normal((T, kv)) * 2).astype(np.float32)   # many ties
+    s[0, 3], s[0, 9] = -0.0, 0.0
+    s[1, [2, 30]] = np.inf
+    s[2, [0, 1, 5]] = -np.inf
+    row_len = np.array([40, 33, 12, 0, 1, 39, 55], np.int32)
+    for k in (1, 7, 12, 39, 40, 45):
+        got = topk_select(s, k, row_len)
+        assert got.shape == (T, k) and got.dtype == np.int32
+        for t in range(T):
+            n = max(0, min(int(row_len[t]), kv))
+            want = _rank_count_select(s[t].tolist(), n, k)
+            assert got[t].tolist() == want, (k, t)
+    got = topk_select(s[:2], 5)                       # no lengths: whole rows
+    assert got[0].tolist() == _rank_count_select(s[0].tolist(), kv, 5)
+
+
+def check_topk_library(topk_select, seed=32):
+    """Distinct scores: the selected set is torch.topk's index set."""
+    rng = np.random.default_rng(seed)
+    T, kv, k = 5, 3000, 2051
+    s = rng.permutation(T * kv).reshape(T, kv).astype(np.float32) / 7.0   # distinct
+    row_len = np.array([3000, 2500, 2052, 2100, 2999], np.int32)
+    got = topk_select(s, k, row_len)
+    for t in range(T):
+        n = int(row_len[t])
+        want = torch.topk(torch.from_numpy(s[t, :n].copy()), k).indices.numpy()
+        assert np.array_equal(got[t], np.sort(want)), t
+
+
+def check_topk_closed_forms(topk_select):
+    kv, k = 50, 8
+    eq = np.zeros((1, kv), np.float32)
+    assert topk_select(eq, k).tolist() == [list(range(k))], "equal scores: lowest positions"
+    up = np.arange(kv, dtype=np.float32)[None]
+    assert topk_select(up, k).tolist() == [list(range(kv - k, kv))], "increasing"
+    assert topk_select(-up, k).tolist() == [list(range(k))], "decreasing"
+    assert topk_select(up, k, np.array([5])).tolist() == [[0, 1, 2, 3, 4, -1, -1, -1]], "short row"
+    assert topk_select(up, k, np.array([0])).tolist() == [[-1] * k], "empty row"
+    z = np.full((1, kv), -1.0, np.float32)
+    z[0, 7], z[0, 2] = -0.0, 0.0
+    assert topk_select(z, 1).tolist() == [[2]], "signed zeros tie"
+    assert topk_select(z, 2).tolist() == [[2, 7]]

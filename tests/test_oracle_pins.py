@@ -461,3 +461,48 @@ def test_pins_catch_decode_mistakes():
     # the unmutated copy passes, so the mutants fail for their mistake alone
     for chk in _decode_checks(_decode_mutant(good)):
         chk()
+
+
+# indexer top-k selection ---------------------------------------------------
+
+def test_topk_rank_count():
+    C.check_topk_rank_count(oracle.topk_select)
+
+
+def test_topk_library():
+    C.check_topk_library(oracle.topk_select)
+
+
+def test_topk_closed_forms():
+    C.check_topk_closed_forms(oracle.topk_select)
+
+
+def _topk_mutant(order_of, n_of=lambda rl, kv: min(int(rl), kv), pad=-1, ascending=True):
+    def run(scores, k, row_len=None):
+        T, kv = scores.shape
+        out = np.full((T, k), pad, np.int32)
+        for t in range(T):
+            n = kv if row_len is None else max(0, n_of(row_len[t], kv))
+            if n <= k:
+                out[t, :n] = np.arange(n)
+                continue
+            sel = np.sort(order_of(scores[t, :n])[:k])
+            out[t] = sel if ascending else sel[::-1]
+        return out
+    return run
+
+
+def test_pins_catch_topk_mistakes():
+    good = lambda v: np.lexsort((np.arange(len(v)), -v.astype(np.float64)))
+    high_ties = lambda v: np.lexsort((-np.arange(len(v)), -v.astype(np.float64)))
+    bits = lambda v: np.lexsort((np.arange(len(v)),
+                                 -np.where(np.signbit(v) & (v == 0), -1e-300, v.astype(np.float64))))
+    mutants = [_topk_mutant(high_ties), _topk_mutant(bits), _topk_mutant(good, ascending=False),
+               _topk_mutant(good, n_of=lambda rl, kv: min(int(rl) + 1, kv)),
+               _topk_mutant(good, n_of=lambda rl, kv: kv), _topk_mutant(good, pad=0)]
+    checks = lambda f: [lambda: C.check_topk_rank_count(f), lambda: C.check_topk_library(f),
+                        lambda: C.check_topk_closed_forms(f)]
+    for m in mutants:
+        assert _fails_some(checks(m))
+    for chk in checks(_topk_mutant(good)):
+        chk()
