@@ -191,7 +191,37 @@ def measure_others(args, sa, torch, stream):
         q, k, v, sidx, 2, sm_scale=c.scale, ws=ws, out=out, lse=lse, stream=stream), w, n)
     r.update({"union_G2_ms": round(ms_u, 4)})
     res["shuffled_slots_same_sets"] = r
-    del q, k, v, idx, sidx, out, lse, ws, ui, ub, ul
+
+    # The indexer's top-k over the same rows (8192 x 32768 fp32 scores with
+    # causal lengths, k 2051), then attention over what it selected. Its rows
+    # come out in ascending position order, so shared tokens do not sit at
+    # the same slot in adjacent rows; the union path, which sorts, shares
+    # gathers anyway.
+    tc = gen.make_config("C1topk", args.seed)
+    sc = torch.from_numpy(tc.scores).cuda()
+    rl = torch.from_numpy(tc.row_len).cuda()
+    tidx = torch.empty((tc.scores.shape[0], tc.k), dtype=torch.int32, device="cuda")
+    ms_t = _events_ms(torch, stream, lambda: sa.indexer_topk(sc, tc.k, row_len=rl, out=tidx,
+                                                             stream=stream), w, n)
+    score_bytes = int(np.minimum(tc.row_len, tc.scores.shape[1]).sum()) * 4
+    r = _rate(score_bytes, ms_t)
+
+    def select_then_union():
+        sa.indexer_topk(sc, tc.k, row_len=rl, out=tidx, stream=stream)
+        sa.sparse_attn_prefill_union(q, k, v, tidx, 2, sm_scale=c.scale, ws=ws, out=out,
+                                     lse=lse, stream=stream)
+
+    def select_then_per_token():
+        sa.indexer_topk(sc, tc.k, row_len=rl, out=tidx, stream=stream)
+        sa.sparse_attn_chunk_prefill(q, k, v, tidx, cu_q1, cu_kv1, sm_scale=c.scale, out=out,
+                                     lse=lse, stream=stream)
+
+    r.update({"score_bytes": score_bytes,
+              "then_union_G2_ms": round(_events_ms(torch, stream, select_then_union, w, n), 4),
+              "then_per_token_ms": round(_events_ms(torch, stream, select_then_per_token, w, n),
+                                         4)})
+    res["indexer_topk"] = r
+    del q, k, v, idx, sidx, out, lse, ws, ui, ub, ul, sc, rl, tidx
 
     # group 12 over two KV heads, 131072-token context
     c = gen.make_config("C2", args.seed)

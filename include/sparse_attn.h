@@ -11,7 +11,8 @@
  *   - union mode: G adjacent rows share one sorted, deduplicated index set
  *     with per-row ownership bits that restore each row's own support;
  *   - the decode-pool page mark and (masked) page split;
- *   - sparse MLA decode over the split pool's FP8 records.
+ *   - sparse MLA decode over the split pool's FP8 records;
+ *   - the indexer's top-k selection, from scores to index rows.
  *
  * Conventions for every entry point:
  *   - Device pointers are owned by the caller. The library allocates and
@@ -298,6 +299,27 @@ sa_status sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_page_desc*
                                    void* ws, size_t ws_bytes, float* out, float* lse,
                                    hipStream_t stream);
 
+/* Indexer top-k selection (sglang PR 37275, "Motivation": the indexer
+ * selects token_topk + compress_ratio - 1 = 2051 token slots per query row,
+ * fewer where the row's visible context is shorter). Row t keeps the k
+ * largest of its first n_t scores, n_t = row_len[t] clamped to [0, kv_len]
+ * (kv_len when row_len is NULL); a larger score wins, equal scores go to the
+ * lower position, and -0 ties with +0. The kept positions are written to
+ * idx[t] in ascending order. A row with n_t <= k writes 0 .. n_t - 1, then
+ * -1 up to k (the padding the attention entry points skip).
+ *
+ * scores  device fp32 [num_rows][score_row_stride], score_row_stride >=
+ *         kv_len; no NaN (rows that start 16-byte aligned are read with
+ *         16-byte loads, others one float at a time)
+ * row_len optional device int32 [num_rows]
+ * idx     device int32 [num_rows][idx_row_stride], idx_row_stride >= k;
+ *         exactly k entries of every row are written
+ * Deterministic; one workgroup per row, no workspace, no host read.
+ */
+sa_status indexer_topk(const float* scores, int64_t score_row_stride, const int32_t* row_len,
+                       int32_t num_rows, int32_t kv_len, int32_t k, int32_t* idx,
+                       int64_t idx_row_stride, hipStream_t stream);
+
 /* Host-only check of an attention descriptor, as sparse_attn_prefill (G=1)
  * or sparse_attn_prefill_union (G>1) would do before launching. Touches no
  * device. Returns SA_OK, SA_OK_FALLBACK (union tile illegal) or an error. */
@@ -317,7 +339,8 @@ typedef enum {
   SA_ENTRY_PAGE_SPLIT = 5,
   SA_ENTRY_CHUNK_PREFILL_UNION = 6,
   SA_ENTRY_DECODE_PAGED = 7,
-  SA_ENTRY_COUNT = 8
+  SA_ENTRY_INDEXER_TOPK = 8,
+  SA_ENTRY_COUNT = 9
 } sa_entry;
 uint64_t sa_call_count(int32_t entry);
 

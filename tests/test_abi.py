@@ -27,6 +27,7 @@ def test_header_declares_the_entry_points():
     for want in ("sparse_attn_prefill", "sparse_attn_chunk_prefill", "sparse_attn_prefill_union",
                  "sparse_attn_union_build", "sparse_attn_union_workspace_bytes", "page_mark",
                  "page_split", "sparse_attn_decode_paged", "sparse_attn_decode_workspace_bytes",
+                 "indexer_topk",
                  "sa_validate_attn", "sa_last_error", "sa_call_count"):
         assert want in names
 
@@ -274,3 +275,17 @@ def test_decode_rejects_on_host():
     before = sa.sa_call_count("sparse_attn_decode_paged")
     assert call(batch=0, w=None, wb=0) == 0                         # nothing to launch, counted
     assert sa.sa_call_count("sparse_attn_decode_paged") == before + 1
+
+
+def test_indexer_topk_rejects_on_host():
+    f = sa.lib().indexer_topk
+    assert f(0x1000, 32768, None, 8, 32768, 0, 0x2000, 2051, None) == -2          # k = 0
+    assert f(0x1000, 32766, None, 8, 32768, 2051, 0x2000, 2051, None) == -2      # stride < kv
+    assert f(0x1000, 32768, None, 8, 32768, 2051, 0x2000, 2050, None) == -2      # idx stride < k
+    assert f(None, 32768, None, 8, 32768, 2051, 0x2000, 2051, None) == -1
+    assert f(0x1002, 32768, None, 8, 32768, 2051, 0x2000, 2051, None) == -2      # misaligned
+    assert f(0x1000, 32768, 0x3002, 8, 32768, 2051, 0x2000, 2051, None) == -2    # row_len align
+    assert f(0x1000, 32768, None, -1, 32768, 2051, 0x2000, 2051, None) == -2
+    before = sa.sa_call_count("indexer_topk")
+    assert f(None, 0, None, 0, 0, 5, None, 5, None) == 0                          # no rows
+    assert sa.sa_call_count("indexer_topk") == before + 1

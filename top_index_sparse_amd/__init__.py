@@ -30,6 +30,7 @@ __all__ = [
     "page_split",
     "sparse_attn_decode_workspace_bytes",
     "sparse_attn_decode_paged",
+    "indexer_topk",
     "sa_validate_attn",
     "sa_last_error",
     "sa_call_count",
@@ -51,7 +52,7 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_OK_FALLBACK", -1: "SA_ERR_NULL", -2: "SA_ERR_
 ENTRIES = {"sparse_attn_prefill": 0, "sparse_attn_chunk_prefill": 1,
            "sparse_attn_union_build": 2, "sparse_attn_prefill_union": 3,
            "page_mark": 4, "page_split": 5, "sparse_attn_chunk_prefill_union": 6,
-           "sparse_attn_decode_paged": 7}
+           "sparse_attn_decode_paged": 7, "indexer_topk": 8}
 
 
 class SparseAttnError(RuntimeError):
@@ -107,6 +108,7 @@ _SIGNATURES = {
     "page_mark": (_I32, [_P, _I64, _I32, _I32, _P, _P]),
     "page_split": (_I32, [ctypes.POINTER(PageDesc), _P, _P, _P, _I32, _P]),
     "sparse_attn_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "indexer_topk": (_I32, [_P, _I64, _P, _I32, _I32, _I32, _P, _I64, _P]),
     "sparse_attn_decode_paged": (_I32, [ctypes.POINTER(AttnDesc), ctypes.POINTER(PageDesc), _P, _P,
                                         _I32, _P, _P, _I32, _P, _SZ, _P, _P, _P]),
     "sa_validate_attn": (ctypes.c_int, [ctypes.POINTER(AttnDesc), _I32]),
@@ -497,3 +499,25 @@ def sparse_attn_decode_paged(q: torch.Tensor, pool: torch.Tensor, idx: torch.Ten
                                         _ptr(out), _ptr(lse), _stream(stream))
     _check(st, "sparse_attn_decode_paged")
     return out, lse
+
+
+def indexer_topk(scores: torch.Tensor, k: int, *, row_len: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Indexer top-k selection (C: indexer_topk). scores [T, kv] fp32 (rows
+    contiguous, any row stride); row_len optional [T] int32
+    visible lengths. Returns idx [T, k] int32: ascending positions, -1 pad."""
+    _need(scores, "scores", torch.float32, 2)
+    _rows_dense(scores, "scores")
+    T, kv = scores.shape
+    if row_len is not None:
+        _need(row_len, "row_len", torch.int32, 1, scores.device)
+        if row_len.shape[0] != T or not row_len.is_contiguous():
+            raise ValueError("row_len must be a contiguous [T] tensor")
+    if out is None:
+        out = torch.empty((T, k), dtype=torch.int32, device=scores.device)
+    _need(out, "out", torch.int32, 2, scores.device)
+    _rows_dense(out, "out")
+    st = lib().indexer_topk(_ptr(scores), scores.stride(0) if T > 0 else kv, _ptr(row_len), T, kv,
+                            int(k), _ptr(out), out.stride(0) if T > 0 else k, _stream(stream))
+    _check(st, "indexer_topk")
+    return out

@@ -542,6 +542,36 @@ sa_status sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_page_desc*
   return ok(SA_ENTRY_DECODE_PAGED);
 }
 
+sa_status indexer_topk(const float* scores, int64_t score_row_stride, const int32_t* row_len,
+                       int32_t num_rows, int32_t kv_len, int32_t k, int32_t* idx,
+                       int64_t idx_row_stride, hipStream_t stream) {
+  g_err[0] = 0;
+  if (num_rows < 0 || kv_len < 0 || k <= 0)
+    return fail(SA_ERR_SHAPE, "num_rows %d, kv_len %d must be >= 0 and k %d > 0", num_rows, kv_len, k);
+  if (score_row_stride < kv_len)
+    return fail(SA_ERR_SHAPE, "score_row_stride %lld < kv_len %d", (long long)score_row_stride,
+                kv_len);
+  if (idx_row_stride < k)
+    return fail(SA_ERR_SHAPE, "idx_row_stride %lld < k %d", (long long)idx_row_stride, k);
+  if (num_rows == 0) return ok(SA_ENTRY_INDEXER_TOPK);
+  if (!scores || !idx) return fail(SA_ERR_NULL, "scores and idx are required");
+  if ((reinterpret_cast<uintptr_t>(scores) & 3u) || (reinterpret_cast<uintptr_t>(idx) & 3u) ||
+      (reinterpret_cast<uintptr_t>(row_len) & 3u))
+    return fail(SA_ERR_SHAPE, "scores, idx and row_len must be 4-byte aligned");
+  sa::TopkParams p{};
+  p.scores = scores;
+  p.score_row_stride = score_row_stride;
+  p.row_len = row_len;
+  p.num_rows = num_rows;
+  p.kv_len = kv_len;
+  p.k = k;
+  p.idx = idx;
+  p.idx_row_stride = idx_row_stride;
+  const hipError_t e = sa::launch_topk(p, stream);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok(SA_ENTRY_INDEXER_TOPK);
+}
+
 sa_status page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src_pages,
                     int32_t src_page_tokens, int8_t* mask, hipStream_t stream) {
   g_err[0] = 0;

@@ -119,6 +119,19 @@ struct PageParams {
   int32_t scale_bytes;
 };
 
+// Indexer top-k: row t keeps the k largest of its first n_t scores
+// (n_t = row_len[t] clamped to [0, kv_len], or kv_len), ascending positions.
+struct TopkParams {
+  const float* scores;        // [num_rows][score_row_stride]
+  int64_t score_row_stride;   // floats
+  const int32_t* row_len;     // nullable
+  int32_t num_rows;
+  int32_t kv_len;
+  int32_t k;
+  int32_t* idx;               // [num_rows][idx_row_stride]
+  int64_t idx_row_stride;
+};
+
 // union: 0 per-token results (ragged when cu_q is set), 1 union lists. The
 // launchers choose the team shape (rows per team, column tiles).
 hipError_t launch_attn_gqa256(AttnParams p, int union_mode, hipStream_t stream);
@@ -135,5 +148,6 @@ hipError_t launch_union_build_ragged(UnionBuildParams p, int32_t* gstart, hipStr
 hipError_t launch_page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src_pages,
                             int32_t src_page_tokens, int8_t* mask, hipStream_t stream);
 hipError_t launch_page_split(const PageParams& p, hipStream_t stream);
+hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
 
 }  // namespace sa
