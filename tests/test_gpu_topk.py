@@ -74,3 +74,13 @@ def test_topk_c1_full_size():
     same = np.mean([len(np.intersect1d(g[t], g[t + 1])) / c.k for t in range(0, 8000, 97)])
     say(f"  mean overlap of adjacent rows {same:.4f}")
     assert 0.95 < same < 0.995
+
+
+def test_topk_counts_past_16_bits():
+    say("[topk] k 66000 of 70000 positions; 70000 equal scores")
+    rng = np.random.default_rng(77)
+    kv, k = 70000, 66000
+    s = (np.round(rng.standard_normal((3, kv)) * 4) / 4).astype(np.float32)
+    s[1] = -2.5
+    _check(s, k, np.array([kv, kv, 69999], np.int32), "k=66000")
+    _check(s[:2], 2051, None, "70000 ties")

@@ -6,18 +6,29 @@
 //
 // gfx950 design: one 1024-thread workgroup per row.
 //   Keys. A score's bits map to a uint32 key whose unsigned order is the
-//   float order (-0 is folded onto +0 first, so the two tie). Rows of at
-//   most 32768 positions keep their keys in registers after one read (up to
-//   32 per thread; 64 would spill at 1024 threads); longer rows read the
-//   scores again for every pass.
-//   Threshold. A radix select over the key's top 11, next 11 and last 10
-//   bits: an LDS histogram of the keys that share the prefix found so far,
-//   then a block-wide scan from the top bin down finds the bin holding the
-//   k-th largest key. It stops early when that whole bin is kept.
-//   Output. The row is walked in position order, 4096 positions at a time
-//   (4 consecutive per thread): a block-wide scan of (kept, tied) counts
-//   gives every thread its output offset, and tied keys are kept while
-//   their rank among the row's ties is below the number still needed.
+//   float order (-0 is folded onto +0 first, so the two tie).
+//   Level 0. An LDS histogram of the keys' top 13 bits (8192 bins, wide
+//   enough that scores crowding a few exponents still spread their atomics)
+//   and a block-wide scan from the top bin down find the bin b0 that holds
+//   the k-th largest key.
+//   Classes. Every element is then above b0 (kept), in b0 (a candidate) or
+//   below (dropped), recorded in two LDS bitmaps by position. Candidates,
+//   usually a few hundred, are compacted into a list in position order;
+//   levels 1 and 2 (11 and 8 more bits) run on that list alone and mark each
+//   candidate kept or tied in two more bitmaps.
+//   Output. Thread j owns bitmap words (positions 32 words at a time, in
+//   order): one block-wide scan of the owners' (kept, tied) counts gives
+//   every owner its first output slot, and it writes its positions in
+//   order, so neighbouring threads write neighbouring slots. An element goes
+//   to (kept before it) + min(tied before it, still needed), and a tie is
+//   kept while fewer than that many ties precede it.
+//   Rows of up to 32768 positions keep their keys in registers from the
+//   single read to the classes; rows up to 65536 read the scores twice.
+//   When the candidates overflow their list (scores crowding one bin),
+//   levels 1 and 2 and the marking read the row again instead. Longer rows
+//   take a generic kernel that runs every level over the row, reads it again
+//   for each pass, and orders the output with per-wave ballots and a scan of
+//   (chunk, wave) totals.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,15 +40,26 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kBins = 2048;
+constexpr int kBins = 8192;     // level 0 digit: the key's top 13 bits
+constexpr int kBatch = 8;       // 4096-position chunks per output batch
+constexpr int kCand = 2048;     // candidate list capacity (a few hundred in practice)
 
 __device__ __forceinline__ uint32_t score_key(uint32_t u) {
   if (u == 0x80000000u) u = 0u;   // -0 ranks as +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// LDS shared by both paths.
+struct TopkLds {
+  uint32_t hist[kBins];
+  uint32_t red[kWaves];
+  uint32_t found[2];
+  uint32_t wsel[kBatch * kWaves + 1];   // output: (chunk, wave) totals, then bases
+  uint32_t wtie[kBatch * kWaves + 1];
+};
+
 // Exclusive prefix over the block of one value per thread; *total gets the
-// block's sum. Two barriers; red holds kWaves words.
+// block's sum. Two barriers.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* red,
                                                          uint32_t* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -61,19 +83,259 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* r
   return before + x - v;
 }
 
-// PER > 0: keys held in registers (n <= kThreads * PER); PER == 0: re-read.
-template <int PER>
-__global__ void __launch_bounds__(kThreads) topk_kernel(TopkParams p) {
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t red[kWaves];
-  __shared__ uint32_t found[2];
-  const int t = blockIdx.x;
+// Prefix over the wave's lanes below this one, and the wave's total, of a
+// count in 0..7 (three ballots; no cross-lane data movement).
+__device__ __forceinline__ void wave_prefix3(uint32_t v, uint32_t* before, uint32_t* total) {
+  uint32_t b = 0, t = 0;
+#pragma unroll
+  for (int bit = 0; bit < 3; ++bit) {
+    const uint64_t m = __ballot((v >> bit) & 1u);
+    b += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))
+         << bit;
+    t += (uint32_t)__popcll(m) << bit;
+  }
+  *before = b;
+  *total = t;
+}
+
+// After a histogram of nb bins: the bin holding the need-th largest counted
+// key (scanning from the top bin down) and how many of that bin are still
+// needed. *whole: the bin is needed entirely. Ends with hist reusable.
+__device__ __forceinline__ void find_bin(TopkLds& L, int nb, uint32_t* need, uint32_t* bin,
+                                         bool* whole) {
   const int tid = threadIdx.x;
+  const int per = nb >= kThreads ? nb / kThreads : 1;
+  const int top = nb - 1 - per * tid;
+  uint32_t mine = 0;
+  for (int j = 0; j < per; ++j) mine += top - j >= 0 ? L.hist[top - j] : 0u;
+  uint32_t tot;
+  uint32_t above = block_exclusive_scan(mine, L.red, &tot);
+  if (above < *need && *need <= above + mine) {
+    for (int j = 0; j < per; ++j) {
+      const uint32_t h = L.hist[top - j];
+      if (*need <= above + h) {
+        L.found[0] = (uint32_t)(top - j);
+        L.found[1] = *need - above;
+        break;
+      }
+      above += h;
+    }
+  }
+  __syncthreads();
+  *bin = L.found[0] & (uint32_t)(nb - 1);   // exactly one thread found it
+  *need = L.found[1];
+  *whole = L.hist[*bin] == *need;
+  __syncthreads();
+}
+
+// Output pass over chunks [0, nchunks) in position order. cls(i, &s, &t)
+// gives this thread's 4 elements of chunk i as kept / tied flags (bit c).
+// need: ties still to keep.
+template <typename Cls>
+__device__ __forceinline__ void write_output(TopkLds& L, int nchunks, uint32_t need, int k,
+                                             int32_t* out, Cls&& cls) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t carry_sel = 0, carry_tie = 0;   // totals of earlier batches
+  for (int b0 = 0; b0 < nchunks; b0 += kBatch) {
+    const int nb = nchunks - b0 < kBatch ? nchunks - b0 : kBatch;
+    uint32_t lane_pre[kBatch], fsel[kBatch], ftie[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      lane_pre[j] = 0;
+      fsel[j] = 0;
+      ftie[j] = 0;
+      if (j < nb) {
+        cls(b0 + j, &fsel[j], &ftie[j]);
+        uint32_t sb, st, tb, tt;
+        wave_prefix3(__popc(fsel[j]), &sb, &st);
+        wave_prefix3(__popc(ftie[j]), &tb, &tt);
+        lane_pre[j] = (sb << 16) | tb;   // each at most 63 * 4
+        if (lane == 0) {
+          L.wsel[j * kWaves + wv] = st;
+          L.wtie[j * kWaves + wv] = tt;
+        }
+      }
+    }
+    __syncthreads();
+    // exclusive scans of the (chunk, wave) totals in position order: wave 0
+    // scans the kept counts, wave 1 the tied ones
+    if (wv < 2) {
+      uint32_t* w = wv == 0 ? L.wsel : L.wtie;
+      const uint32_t carry = wv == 0 ? carry_sel : carry_tie;
+      const int e = 2 * lane;   // entries e, e+1 of kBatch * kWaves = 128
+      const uint32_t a = e < nb * kWaves ? w[e] : 0u;
+      const uint32_t b = e + 1 < nb * kWaves ? w[e + 1] : 0u;
+      uint32_t x = a + b;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      const uint32_t ex = x - a - b;
+      w[e] = carry + ex;
+      w[e + 1] = carry + ex + a;
+      if (lane == 63) w[kBatch * kWaves] = carry + x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (j < nb && (fsel[j] | ftie[j])) {
+        uint32_t kept = L.wsel[j * kWaves + wv] + (lane_pre[j] >> 16);
+        uint32_t tied = L.wtie[j * kWaves + wv] + (lane_pre[j] & 0xffffu);
+        const int pos = 4 * ((b0 + j) * kThreads + tid);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          // (the counts give exactly k writes; o < k keeps every store in the row)
+          const uint32_t o = kept + (tied < need ? tied : need);
+          const bool w = ((fsel[j] >> c) & 1u) || (((ftie[j] >> c) & 1u) && tied < need);
+          if (w && o < (uint32_t)k) out[o] = pos + c;
+          kept += (fsel[j] >> c) & 1u;
+          tied += (ftie[j] >> c) & 1u;
+        }
+      }
+    }
+    carry_sel = L.wsel[kBatch * kWaves];
+    carry_tie = L.wtie[kBatch * kWaves];
+    __syncthreads();   // the totals are rewritten by the next batch
+  }
+}
+
+__device__ __forceinline__ void load4_keys(const float* row, int n, bool vec, int i,
+                                           uint32_t k4[4]) {
+  const int pos = 4 * (i * kThreads + (int)threadIdx.x);
+  if (vec && pos + 3 < n) {
+    const float4 v = *reinterpret_cast<const float4*>(row + pos);
+    k4[0] = score_key(__float_as_uint(v.x));
+    k4[1] = score_key(__float_as_uint(v.y));
+    k4[2] = score_key(__float_as_uint(v.z));
+    k4[3] = score_key(__float_as_uint(v.w));
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) k4[c] = pos + c < n ? score_key(__float_as_uint(row[pos + c])) : 0u;
+  }
+}
+
+// Generic path, any row length: every level and the output re-read the
+// row's scores (0 keys = past the row; no score maps to 0).
+__device__ __forceinline__ void select_generic(TopkLds& L, const float* row, int n, bool vec, int k,
+                               int32_t* out) {
+  const int tid = threadIdx.x;
+  const int nchunks = (n + 4 * kThreads - 1) / (4 * kThreads);
+  uint32_t prefix = 0;
+  int shift = 32;
+  uint32_t need = (uint32_t)k;
+#pragma unroll 1
+  for (int level = 0; level < 3; ++level) {
+    const int bits = level == 0 ? 13 : (level == 1 ? 11 : 8);
+    const int sh = level == 0 ? 19 : (level == 1 ? 8 : 0);
+    const int nb = 1 << bits;
+    for (int b = tid; b < nb; b += kThreads) L.hist[b] = 0u;
+    __syncthreads();
+    for (int i = 0; i < nchunks; ++i) {
+      uint32_t k4[4];
+      load4_keys(row, n, vec, i, k4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t kk = k4[c];
+        if (kk != 0u && (shift == 32 || (kk >> shift) == prefix))
+          atomicAdd(&L.hist[(kk >> sh) & (uint32_t)(nb - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    uint32_t bin;
+    bool whole;
+    find_bin(L, nb, &need, &bin, &whole);
+    prefix = (shift == 32 ? 0u : prefix << bits) | bin;
+    shift = sh;
+    if (whole) break;
+  }
+  write_output(L, nchunks, need, k, out, [&](int i, uint32_t* fs, uint32_t* ft) {
+    uint32_t k4[4];
+    load4_keys(row, n, vec, i, k4);
+    uint32_t s = 0, t = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t pk = k4[c] >> shift;
+      s |= (uint32_t)(k4[c] != 0u && pk > prefix) << c;
+      t |= (uint32_t)(k4[c] != 0u && pk == prefix) << c;
+    }
+    *fs = s;
+    *ft = t;
+  });
+}
+
+// Exclusive prefixes over the block of two values per thread; *t1, *t2
+// get the block's sums. Two barriers; red holds 2 * kWaves words.
+__device__ __forceinline__ void block_exclusive_scan2(uint32_t v1, uint32_t v2, uint32_t* red,
+                                                      uint32_t* e1, uint32_t* e2, uint32_t* t1,
+                                                      uint32_t* t2) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t x1 = v1, x2 = v2;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y1 = __shfl_up(x1, o), y2 = __shfl_up(x2, o);
+    if (lane >= o) {
+      x1 += y1;
+      x2 += y2;
+    }
+  }
+  if (lane == 63) {
+    red[wv] = x1;
+    red[kWaves + wv] = x2;
+  }
+  __syncthreads();
+  uint32_t b1 = 0, b2 = 0, a1 = 0, a2 = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t s1 = red[w], s2 = red[kWaves + w];
+    b1 += w < wv ? s1 : 0u;
+    b2 += w < wv ? s2 : 0u;
+    a1 += s1;
+    a2 += s2;
+  }
+  __syncthreads();
+  *e1 = b1 + x1 - v1;
+  *e2 = b2 + x2 - v2;
+  *t1 = a1;
+  *t2 = a2;
+}
+
+// Fast path for rows of at most kThreads * PER positions. Position bitmaps
+// in LDS (bit j of word w = position 32 w + j): kept by level 0 (above the
+// threshold bin, or all of a bin needed whole), candidates (in that bin),
+// and the candidates kept or tied after levels 1 and 2.
+template <int PER>
+struct FastLds : TopkLds {
+  static constexpr int kWords = PER * kThreads / 32;
+  uint32_t amap[kWords];
+  uint32_t cmap[kWords];
+  uint32_t selb[kWords];
+  uint32_t tieb[kWords];
+  uint32_t red2[2 * kWaves];
+  uint32_t ckey[kCand];
+  int32_t cpos[kCand];
+};
+
+// Every row's visible length and, when it exceeds k, the selection.
+__device__ __forceinline__ int row_length(const TopkParams& p, int t) {
   int n = p.kv_len;
   if (p.row_len) {
     const int r = p.row_len[t];
     n = r < 0 ? 0 : (r < n ? r : n);
   }
+  return n;
+}
+
+// REG: the keys stay in registers from the single read to the classes.
+template <int PER, bool REG>
+__global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
+  __shared__ FastLds<PER> L;
+  constexpr int NCH = PER / 4;                      // 4096-position chunks
+  constexpr int NWORDS = FastLds<PER>::kWords;      // bitmap words
+  constexpr int WPT = NWORDS >= kThreads ? NWORDS / kThreads : 1;   // words per owner
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = row_length(p, t);
   int32_t* out = p.idx + (int64_t)t * p.idx_row_stride;
   if (n <= p.k) {   // every visible position, then padding
     for (int j = tid; j < p.k; j += kThreads) out[j] = j < n ? j : -1;
@@ -81,127 +343,207 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkParams p) {
   }
   const float* row = p.scores + (int64_t)t * p.score_row_stride;
   const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;   // 16-byte loads
-  const int nchunks = PER > 0 ? PER / 4 : (n + 4 * kThreads - 1) / (4 * kThreads);
 
-  // keys of chunk i: positions 4 (i kThreads + tid) .. +3; 0 = past the row
-  // (no score maps to 0: only NaN bit patterns would)
-  auto load4 = [&](int i, uint32_t k4[4]) {
-    const int pos = 4 * (i * kThreads + tid);
-    if (vec && pos + 3 < n) {
-      const float4 v = *reinterpret_cast<const float4*>(row + pos);
-      k4[0] = score_key(__float_as_uint(v.x));
-      k4[1] = score_key(__float_as_uint(v.y));
-      k4[2] = score_key(__float_as_uint(v.z));
-      k4[3] = score_key(__float_as_uint(v.w));
-    } else {
+  // ---- level 0 --------------------------------------------------------------
+  for (int b = tid; b < kBins; b += kThreads) L.hist[b] = 0u;
+  for (int w = tid; w < NWORDS; w += kThreads) L.amap[w] = L.cmap[w] = L.selb[w] = L.tieb[w] = 0u;
+  uint32_t kreg[REG ? PER : 1];
+  if constexpr (REG) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) k4[c] = pos + c < n ? score_key(__float_as_uint(row[pos + c])) : 0u;
-    }
-  };
-  uint32_t kreg[PER > 0 ? PER : 1];
-  if constexpr (PER > 0) {
-#pragma unroll
-    for (int i = 0; i < PER / 4; ++i) load4(i, &kreg[4 * i]);
+    for (int i = 0; i < NCH; ++i) load4_keys(row, n, vec, i, &kreg[4 * i]);
   }
-  auto chunk = [&](int i, uint32_t k4[4]) {
-    if constexpr (PER > 0) {
+  auto keys = [&](int i, uint32_t k4[4]) {
+    if constexpr (REG) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) k4[c] = kreg[4 * i + c];
     } else {
-      load4(i, k4);
+      load4_keys(row, n, vec, i, k4);
     }
   };
-  // every chunk in order (unrolled when the keys are registers)
-  auto for_chunks = [&](auto&& body) {
-    if constexpr (PER > 0) {
+  __syncthreads();
+  // chunks in groups of 8; re-read groups are kept apart so that at most 8
+  // chunks of loads are in flight. Past-the-row keys (0) are not counted:
+  // one bin taking thousands of same-address atomics would serialise them.
 #pragma unroll
-      for (int i = 0; i < PER / 4; ++i) body(i);
-    } else {
-      for (int i = 0; i < nchunks; ++i) body(i);
-    }
-  };
-
-  // ---- threshold: prefix of the k-th largest key ------------------------
-  uint32_t prefix = 0;   // bins found so far
-  int shift = 32;        // keys are compared as key >> shift against prefix
-  uint32_t need = (uint32_t)p.k;
-#pragma unroll 1
-  for (int level = 0; level < 3; ++level) {
-    const int sh = level == 0 ? 21 : (level == 1 ? 10 : 0);
-    const uint32_t mask = level == 2 ? 0x3ffu : 0x7ffu;
-    hist[tid] = 0u;
-    hist[tid + kThreads] = 0u;
-    __syncthreads();
-    for_chunks([&](int i) {
+  for (int g = 0; g < (NCH + 7) / 8; ++g) {
+#pragma unroll
+    for (int i8 = 0; i8 < (NCH < 8 ? NCH : 8); ++i8) {
+      const int i = 8 * g + i8;
       uint32_t k4[4];
-      chunk(i, k4);
+      keys(i, k4);
+      if ((i + 1) * 4 * kThreads <= n) {   // the whole chunk is inside the row
+#pragma unroll
+        for (int c = 0; c < 4; ++c) atomicAdd(&L.hist[k4[c] >> 19], 1u);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (k4[c] != 0u) atomicAdd(&L.hist[k4[c] >> 19], 1u);
+      }
+    }
+    if (!REG) __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+  uint32_t need = (uint32_t)p.k, b0;
+  bool whole0;
+  find_bin(L, kBins, &need, &b0, &whole0);
+
+  // ---- classes into the position bitmaps -------------------------------------
+  // chunk i covers positions 4 (i kThreads + tid) .. +3: one nibble of word
+  // (i kThreads + tid) / 8, shared with the 7 neighbouring threads
+#pragma unroll
+  for (int g = 0; g < (NCH + 7) / 8; ++g) {
+#pragma unroll
+    for (int i8 = 0; i8 < (NCH < 8 ? NCH : 8); ++i8) {
+      const int i = 8 * g + i8;
+      uint32_t k4[4];
+      keys(i, k4);
+      uint32_t a = 0, cm = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t kk = k4[c];
-        if (kk != 0u && (shift == 32 || (kk >> shift) == prefix))
-          atomicAdd(&hist[(kk >> sh) & mask], 1u);
+        const uint32_t d = k4[c] >> 19;   // (0 keys fall below b0)
+        a |= (uint32_t)(d > b0 || (whole0 && d == b0)) << c;
+        cm |= (uint32_t)(!whole0 && d == b0) << c;
       }
-    });
-    __syncthreads();
-    // bins 2047 - 2 tid and 2046 - 2 tid, scanned from the top bin down
-    const uint32_t ha = hist[kBins - 1 - 2 * tid], hb = hist[kBins - 2 - 2 * tid];
-    uint32_t tot;
-    const uint32_t above = block_exclusive_scan(ha + hb, red, &tot);
-    if (above < need && need <= above + ha) {
-      found[0] = kBins - 1 - 2 * tid;
-      found[1] = need - above;
-    } else if (above + ha < need && need <= above + ha + hb) {
-      found[0] = kBins - 2 - 2 * tid;
-      found[1] = need - above - ha;
+      const int word = (i * kThreads + tid) >> 3;
+      const uint32_t sh = 4u * (uint32_t)(tid & 7);
+      if (a) atomicOr(&L.amap[word], a << sh);
+      if (cm) atomicOr(&L.cmap[word], cm << sh);
+    }
+    if (!REG) __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+
+  // ---- levels 1 and 2 on the candidates (or, on overflow, the row) -----------
+  uint32_t tie_need = 0;
+  if (!whole0) {
+    // candidate list, compacted in position order by the bitmap words' owners
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int w = tid * WPT + j;
+      mine += w < NWORDS ? __popc(L.cmap[w]) : 0u;
+    }
+    uint32_t nc;
+    uint32_t off = block_exclusive_scan(mine, L.red, &nc);
+    const bool spill = nc > (uint32_t)kCand;   // candidates overflow their list
+    if (!spill && mine) {
+#pragma unroll
+      for (int j = 0; j < WPT; ++j) {
+        const int w = tid * WPT + j;
+        uint32_t m = w < NWORDS ? L.cmap[w] : 0u;
+        while (m) {
+          const int pos = 32 * w + __builtin_ctz(m);
+          m &= m - 1u;
+          L.ckey[off] = score_key(__float_as_uint(row[pos]));
+          L.cpos[off] = pos;
+          ++off;
+        }
+      }
     }
     __syncthreads();
-    const uint32_t bin = found[0] & (kBins - 1);   // exactly one thread found it
-    need = found[1];
-    prefix = (shift == 32 ? 0u : prefix << (level == 2 ? 10 : 11)) | bin;
-    shift = sh;
-    const bool whole = hist[bin] == need;   // the bin is kept entirely
-    __syncthreads();                        // hist and found are reused
-    if (whole) break;
+    uint32_t prefix = b0;
+    int shift = 19;
+#pragma unroll 1
+    for (int level = 1; level < 3; ++level) {
+      const int bits = level == 1 ? 11 : 8;
+      const int sh = level == 1 ? 8 : 0;
+      const int nb = 1 << bits;
+      for (int b = tid; b < nb; b += kThreads) L.hist[b] = 0u;
+      __syncthreads();
+      if (!spill) {
+        for (uint32_t c = tid; c < nc; c += kThreads) {
+          const uint32_t kk = L.ckey[c];
+          if ((kk >> shift) == prefix) atomicAdd(&L.hist[(kk >> sh) & (uint32_t)(nb - 1)], 1u);
+        }
+      } else {
+#pragma unroll 1
+        for (int i = 0; i < NCH; ++i) {
+          uint32_t k4[4];
+          load4_keys(row, n, vec, i, k4);
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (k4[c] != 0u && (k4[c] >> shift) == prefix)
+              atomicAdd(&L.hist[(k4[c] >> sh) & (uint32_t)(nb - 1)], 1u);
+        }
+      }
+      __syncthreads();
+      uint32_t bin;
+      bool whole;
+      find_bin(L, nb, &need, &bin, &whole);
+      prefix = (prefix << bits) | bin;
+      shift = sh;
+      if (whole) break;
+    }
+    // mark the candidates: kept above the threshold prefix, tied at it
+    auto mark = [&](uint32_t kk, int pos) {
+      const uint32_t pk = kk >> shift;
+      if (pk > prefix) atomicOr(&L.selb[pos >> 5], 1u << (pos & 31));
+      else if (pk == prefix) atomicOr(&L.tieb[pos >> 5], 1u << (pos & 31));
+    };
+    if (!spill) {
+      for (uint32_t c = tid; c < nc; c += kThreads) mark(L.ckey[c], L.cpos[c]);
+    } else {
+#pragma unroll 1
+      for (int i = 0; i < NCH; ++i) {
+        uint32_t k4[4];
+        load4_keys(row, n, vec, i, k4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (k4[c] != 0u && (k4[c] >> 19) == b0) mark(k4[c], 4 * (i * kThreads + tid) + c);
+      }
+    }
+    tie_need = need;
+    __syncthreads();
   }
 
-  // ---- output in position order ------------------------------------------
-  uint32_t written = 0, ties_before = 0;
-  for_chunks([&](int i) {
-    uint32_t k4[4];
-    chunk(i, k4);
-    uint32_t nsel = 0, ntie = 0;
+  // ---- output from the bitmaps, in position order ------------------------------
+  // An element goes to (kept before it) + min(tied before it, tie_need); a
+  // tie is kept while fewer than tie_need ties precede it.
+  uint32_t ksel[WPT], ktie[WPT], ns = 0, nt = 0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t pk = k4[c] >> shift;
-      nsel += k4[c] != 0u && pk > prefix;
-      ntie += k4[c] != 0u && pk == prefix;
-    }
-    uint32_t tot;
-    const uint32_t pre = block_exclusive_scan((nsel << 16) | ntie, red, &tot);
-    const uint32_t quota = need > ties_before ? need - ties_before : 0u;
-    uint32_t tie_rank = pre & 0xffffu;
-    uint32_t o = written + (pre >> 16) + (tie_rank < quota ? tie_rank : quota);
-    const int pos = 4 * (i * kThreads + tid);
+  for (int j = 0; j < WPT; ++j) {
+    const int w = tid * WPT + j;
+    const uint32_t am = w < NWORDS ? L.amap[w] : 0u;
+    const uint32_t cm = w < NWORDS ? L.cmap[w] : 0u;
+    ksel[j] = am | (cm & (w < NWORDS ? L.selb[w] : 0u));
+    ktie[j] = cm & (w < NWORDS ? L.tieb[w] : 0u);
+    ns += __popc(ksel[j]);
+    nt += __popc(ktie[j]);
+  }
+  uint32_t kept, tied, ts, tt;
+  block_exclusive_scan2(ns, nt, L.red2, &kept, &tied, &ts, &tt);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t pk = k4[c] >> shift;
-      if (k4[c] == 0u) continue;
+  for (int j = 0; j < WPT; ++j) {
+    const int w = tid * WPT + j;
+    uint32_t m = ksel[j] | ktie[j];
+    while (m) {
+      const int b = __builtin_ctz(m);
+      m &= m - 1u;
       // (the counts give exactly k writes; o < k keeps every store in the row)
-      if (pk > prefix) {
-        if (o < (uint32_t)p.k) out[o] = pos + c;
-        ++o;
-      } else if (pk == prefix) {
-        if (tie_rank < quota) {
-          if (o < (uint32_t)p.k) out[o] = pos + c;
-          ++o;
-        }
-        ++tie_rank;
+      const uint32_t o = kept + (tied < tie_need ? tied : tie_need);
+      if ((ksel[j] >> b) & 1u) {
+        if (o < (uint32_t)p.k) out[o] = 32 * w + b;
+        ++kept;
+      } else {
+        if (tied < tie_need && o < (uint32_t)p.k) out[o] = 32 * w + b;
+        ++tied;
       }
     }
-    const uint32_t tsel = tot >> 16, ttie = tot & 0xffffu;
-    written += tsel + (ttie < quota ? ttie : quota);
-    ties_before += ttie;
-  });
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) topk_generic_kernel(TopkParams p) {
+  __shared__ TopkLds L;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = row_length(p, t);
+  int32_t* out = p.idx + (int64_t)t * p.idx_row_stride;
+  if (n <= p.k) {
+    for (int j = tid; j < p.k; j += kThreads) out[j] = j < n ? j : -1;
+    return;
+  }
+  const float* row = p.scores + (int64_t)t * p.score_row_stride;
+  select_generic(L, row, n, (reinterpret_cast<uintptr_t>(row) & 15u) == 0, p.k, out);
 }
 
 }  // namespace
@@ -210,13 +552,15 @@ hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
   const int kv = p.kv_len;
   const dim3 grid((unsigned)p.num_rows), block(kThreads);
   if (kv <= 4 * kThreads)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((topk_fast_kernel<4, true>), grid, block, 0, stream, p);
   else if (kv <= 16 * kThreads)
-    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((topk_fast_kernel<16, true>), grid, block, 0, stream, p);
   else if (kv <= 32 * kThreads)
-    hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((topk_fast_kernel<32, true>), grid, block, 0, stream, p);
+  else if (kv <= 64 * kThreads)
+    hipLaunchKernelGGL((topk_fast_kernel<64, false>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL(topk_kernel<0>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL(topk_generic_kernel, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
