@@ -165,6 +165,23 @@ def measure_others(args, sa, torch, stream):
     per_token_bytes = gathered_bytes(c)
     cu_q1 = torch.tensor([0, c.num_rows], dtype=torch.int32, device="cuda")
     cu_kv1 = torch.tensor([0, c.kv_len], dtype=torch.int64, device="cuda")
+
+    # The headline with cold caches: every call reads the next of 10 copies
+    # of K and V (335 MB in all, more than the 256 MB Infinity Cache), so each
+    # call starts with its K/V rows in HBM only.
+    copies = [(k.clone(), v.clone()) for _ in range(10)]
+    turn = [0]
+
+    def rotating():
+        kk, vv = copies[turn[0] % len(copies)]
+        turn[0] += 1
+        sa.sparse_attn_chunk_prefill(q, kk, vv, idx, cu_q1, cu_kv1, sm_scale=c.scale, out=out,
+                                     lse=lse, stream=stream)
+
+    r = _rate(per_token_bytes, _events_ms(torch, stream, rotating, 10, 20))
+    r["kv_copies"] = len(copies)
+    res["headline_cold_kv"] = r
+    del copies
     ws = torch.empty(sa.sparse_attn_union_workspace_bytes(c.num_rows, c.topk, 2),
                      dtype=torch.uint8, device="cuda")
     ui, ub, ul = sa.sparse_attn_union_build(idx, c.kv_len, 2, ws=ws, stream=stream)
