@@ -413,7 +413,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(rows and KV heads shard with no exchange; see the design notes). "
+              "(query rows and KV heads would shard across GPUs with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

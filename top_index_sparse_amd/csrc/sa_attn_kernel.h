@@ -378,20 +378,23 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
       if (shi >= 0) td.kd[5] = ld16(kwb + join64(pick(klo, is), shi) + 512);
       return;
     }
-    if (VKLDS) {
-      // Linear chunk order: load q covers chunks 64q .. 64q+63 of the tile's
-      // 16 slot rows (CPR chunks each), so consecutive lanes read
-      // consecutive 16-byte pieces of the same row. Slot s's offset sits in
-      // the lanes of quad s%4 of lane group s/4; the permutes run with every
-      // lane active.
+    if constexpr (VKLDS) {
+      // Lane group g gathers its own slots 4g..4g+3 (their offsets arrive by
+      // row broadcast): load q of lane n takes chunk c = 16q + n of the
+      // group's 4 * CPR chunks, i.e. chunk c % CPR of slot 4g + c / CPR, so
+      // sixteen lanes read 256 consecutive bytes of a row, and the sixteen
+      // chunks of one load span at most two slots (CPR > 16).
+      static_assert(CPR > 16 && 4 * CPR == 16 * KSTEPS, "MLA slice chunks");
+      int klo[4];
+      row_bcast4((int)koff, klo);
 #pragma unroll
       for (int q = 0; q < KSTEPS; ++q) {
-        const int e = 64 * q + lane;
-        const int slot = e / CPR;
-        const int ch = e - slot * CPR;
-        const int src = (16 * (slot >> 2) + 4 * (slot & 3)) << 2;
-        const int lo = __builtin_amdgcn_ds_bpermute(src, (int)koff);
-        const int hi = __builtin_amdgcn_ds_bpermute(src, (int)(koff >> 32));
+        const int i0 = (16 * q) / CPR;              // the load's first slot
+        const int c = 16 * q + n;
+        const bool nx = i0 < 3 && c >= CPR * (i0 + 1);   // this lane is in the next slot
+        const int lo = nx ? klo[i0 < 3 ? i0 + 1 : 3] : klo[i0];
+        const int hi = nx ? khi[i0 < 3 ? i0 + 1 : 3] : khi[i0];
+        const int ch = c - CPR * (nx ? i0 + 1 : i0);
         const int d = ch < MAIN / 8 ? split * MAIN + 8 * ch : DV + split * ROPE + 8 * (ch - MAIN / 8);
         if (hi >= 0) td.kd[q] = ld16(kwb + join64(lo, hi) + 2 * d);
       }
@@ -455,12 +458,14 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
         *reinterpret_cast<u32x4_t*>(row + 16) = (u32x4_t){b[4], b[5], b[6], b[7]};
       }
       *reinterpret_cast<u32x4_t*>(lk + (4 * g + (n >> 2)) * KROW + 16 * (MAIN / 8 + (n & 3))) = td.kd[4];
-    } else if (VKLDS) {
+    } else if constexpr (VKLDS) {
+      // chunk c = 16q + n of group g's slots (the gather's order)
 #pragma unroll
       for (int q = 0; q < KSTEPS; ++q) {
-        const int e = 64 * q + lane;
-        const int slot = e / CPR;
-        *reinterpret_cast<u32x4_t*>(lk + slot * KROW + 16 * (e - slot * CPR)) = td.kd[q];
+        const int i0 = (16 * q) / CPR;
+        const int c = 16 * q + n;
+        const int i = i0 < 3 && c >= CPR * (i0 + 1) ? i0 + 1 : i0;
+        *reinterpret_cast<u32x4_t*>(lk + (4 * g + i) * KROW + 16 * (c - CPR * i)) = td.kd[q];
       }
     } else {
       // write slot 4g+i, bytes 256h + 16m; read slot m, bytes 64s + 16g. The
