@@ -197,7 +197,7 @@ sa_status sparse_attn_prefill_union(const sa_attn_desc* desc, const void* q, con
  * int32 first group id per request [num_reqs + 1], then int32 union_idx
  * [groups][stride], uint8 union_bits [groups][stride], int32 union_len
  * [groups] (the union_build layout per group, request-local indices; groups
- * listed request by request). */
+ * listed request by request; entries past union_len[g] are not written). */
 size_t sparse_attn_chunk_union_workspace_bytes(int32_t total_q, int32_t num_reqs, int32_t topk,
                                                int32_t G);
 

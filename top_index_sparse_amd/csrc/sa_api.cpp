@@ -343,6 +343,7 @@ sa_status sparse_attn_union_build(const int32_t* idx, int64_t idx_row_stride, in
   b.union_bits = union_bits;
   b.union_len = union_len;
   b.union_stride = (int64_t)G * topk;
+  b.fill_tail = 1;   // the documented -1 / 0 fill after union_len
   const hipError_t e = sa::launch_union_build(b, stream);
   if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok(SA_ENTRY_UNION_BUILD);

@@ -83,6 +83,7 @@ struct UnionBuildParams {
   int32_t num_reqs;
   int32_t num_groups;         // groups launched (an upper bound when ragged)
   int32_t plane_words;        // 32-token words per member per bit-plane chunk
+  int32_t fill_tail;          // write -1 / 0 after union_len up to G * topk
 };
 
 // Ragged union groups: ids [gstart[r], gstart[r+1]) belong to request r,

@@ -219,7 +219,7 @@ __global__ void __launch_bounds__(kMergeThreads) union_merge_kernel(UnionBuildPa
     __syncthreads();
   }
   const int len = carry_s;
-  for (int64_t r = len + threadIdx.x; r < width; r += kMergeThreads) {
+  for (int64_t r = len + threadIdx.x; p.fill_tail && r < width; r += kMergeThreads) {
     uidx[r] = -1;
     ubits[r] = 0;
   }
@@ -399,7 +399,7 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuild
     __syncthreads();   // the planes are cleared for the next chunk
   }
   const int64_t width = (int64_t)p.G * p.topk;
-  for (int64_t r = len + tid; r < width; r += kBitmapThreads) {
+  for (int64_t r = len + tid; p.fill_tail && r < width; r += kBitmapThreads) {
     uidx[r] = -1;
     ubits[r] = 0;
   }
