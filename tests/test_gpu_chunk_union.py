@@ -83,6 +83,22 @@ def test_chunk_union_small_ragged(G):
     check_close(out, lse, ro, rl, f"chunk union G={G}")
 
 
+@pytest.mark.parametrize("R", [256, 300])
+def test_chunk_union_many_requests(R):
+    # the build stages up to 256 requests' first group ids in LDS and
+    # searches the rest in global memory: both sides of that limit
+    say(f"[chunk union] {R} small requests, G=2")
+    rng = np.random.default_rng(R)
+    qlens = rng.integers(0, 5, R)
+    ctxs = rng.integers(6, 40, R)
+    c = _ragged(R, list(qlens), list(ctxs), 6, 256, 256, 8, swap=0.3)
+    out, lse, st, (ui, ub, ul, gr), _ = _run(c, 2)
+    assert st == sa.SA_OK
+    ro, rl = oracle.chunk_union_attention(c["q"], c["k"], c["v"], ui, ub, ul, gr, c["cu_q"],
+                                          c["cu_kv"], 2, num_kv_heads=1, scale=c["scale"])
+    check_close(out, lse, ro, rl, f"chunk union {R} requests")
+
+
 def test_chunk_union_long_context_chunked_planes():
     # ragged builds keep 16 KB of bit planes: 32768 tokens per chunk at G = 4,
     # so a 300000-token request takes ten chunks; indices spread over it all

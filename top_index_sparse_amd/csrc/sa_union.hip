@@ -228,16 +228,17 @@ __global__ void __launch_bounds__(kMergeThreads) union_merge_kernel(UnionBuildPa
 
 constexpr int kBitmapThreads = 256;
 constexpr int kMaxMembers = 8;
+constexpr int kStagedReqs = 256;   // ragged build: requests whose group starts go to LDS
 constexpr int kRaggedPlaneBytes = 16384;
 
 // Block-wide exclusive scan of per-thread counts (thread order), for every
 // bucket at once; returns each bucket's total in tot.
-__device__ __forceinline__ void scan_buckets(const int cnt[kMaxMembers], int excl[kMaxMembers],
-                                             int tot[kMaxMembers],
-                                             int32_t (*wave_tot)[kMaxMembers]) {
+template <int M>
+__device__ __forceinline__ void scan_buckets(const int cnt[M], int excl[M], int tot[M],
+                                             int32_t (*wave_tot)[M]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < kMaxMembers; ++j) {
+  for (int j = 0; j < M; ++j) {
     int incl = cnt[j];
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -249,7 +250,7 @@ __device__ __forceinline__ void scan_buckets(const int cnt[kMaxMembers], int exc
   }
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < kMaxMembers; ++j) {
+  for (int j = 0; j < M; ++j) {
     int before = 0, total = 0;
 #pragma unroll
     for (int w = 0; w < kBitmapThreads / 64; ++w) {
@@ -267,16 +268,27 @@ __device__ __forceinline__ void scan_buckets(const int cnt[kMaxMembers], int exc
 // of 32 * plane_words tokens (one chunk whenever the planes fit); with more
 // than one chunk a first pass counts every bucket so that the second can
 // place each chunk's tokens after the earlier chunks'.
-template <bool RAGGED>
+// M: member capacity (2, 4 or 8, at least G), the size of the per-member
+// registers and scans.
+template <bool RAGGED, int M>
 __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuildParams p) {
   extern __shared__ uint32_t planes[];   // [members][plane_words]
-  __shared__ int32_t wave_tot[kBitmapThreads / 64][kMaxMembers];
+  __shared__ int32_t wave_tot[kBitmapThreads / 64][M];
   const int gi = blockIdx.x;
   const int tid = threadIdx.x;
   int first, members, kv_len;
   if (RAGGED) {
+    // the group's request: a binary search of the first group ids, staged
+    // in LDS (one round trip instead of one per search step)
+    __shared__ int32_t gs[kStagedReqs + 1];
+    const int32_t* starts = p.gstart;
+    if (p.num_reqs <= kStagedReqs) {
+      for (int r = tid; r <= p.num_reqs; r += kBitmapThreads) gs[r] = p.gstart[r];
+      __syncthreads();
+      starts = gs;
+    }
     int64_t kv_base;
-    if (!ragged_group(p.gstart, p.cu_q, p.cu_kv, p.num_reqs, p.G, gi, first, members, kv_base,
+    if (!ragged_group(starts, p.cu_q, p.cu_kv, p.num_reqs, p.G, gi, first, members, kv_base,
                       kv_len))
       return;
   } else {
@@ -309,13 +321,13 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuild
   };
   // Each thread owns a contiguous range of words; counts its tokens per
   // bucket (the bucket of a token is its lowest owning member).
-  auto count = [&](int W, int w0, int w1, int cnt[kMaxMembers]) {
+  auto count = [&](int W, int w0, int w1, int cnt[M]) {
 #pragma unroll
-    for (int j = 0; j < kMaxMembers; ++j) cnt[j] = 0;
+    for (int j = 0; j < M; ++j) cnt[j] = 0;
     for (int w = w0; w < w1; ++w) {
       uint32_t seen = 0u;
 #pragma unroll
-      for (int j = 0; j < kMaxMembers; ++j) {
+      for (int j = 0; j < M; ++j) {
         if (j < members) {
           const uint32_t b = planes[j * W + w];
           cnt[j] += __popc(b & ~seen);
@@ -331,55 +343,55 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuild
     w1 = min(W, w0 + wpt);
   };
 
-  int total[kMaxMembers];
+  int total[M];
 #pragma unroll
-  for (int j = 0; j < kMaxMembers; ++j) total[j] = 0;
+  for (int j = 0; j < M; ++j) total[j] = 0;
   if (nchunks > 1) {
     for (int c = 0; c < nchunks; ++c) {
       const int W = words(c);
-      int w0, w1, cnt[kMaxMembers], excl[kMaxMembers], tot[kMaxMembers];
+      int w0, w1, cnt[M], excl[M], tot[M];
       range(W, w0, w1);
       mark(c * cap, W);
       count(W, w0, w1, cnt);
-      scan_buckets(cnt, excl, tot, wave_tot);
+      scan_buckets<M>(cnt, excl, tot, wave_tot);
 #pragma unroll
-      for (int j = 0; j < kMaxMembers; ++j) total[j] += tot[j];
+      for (int j = 0; j < M; ++j) total[j] += tot[j];
     }
   }
-  int base[kMaxMembers], carry[kMaxMembers];
+  int base[M], carry[M];
   int len = 0;
 #pragma unroll
-  for (int j = 0; j < kMaxMembers; ++j) carry[j] = 0;
+  for (int j = 0; j < M; ++j) carry[j] = 0;
   for (int c = 0; c < nchunks; ++c) {
     const int W = words(c);
     const int c0 = c * cap;
-    int w0, w1, cnt[kMaxMembers], excl[kMaxMembers], tot[kMaxMembers];
+    int w0, w1, cnt[M], excl[M], tot[M];
     range(W, w0, w1);
     mark(c0, W);
     count(W, w0, w1, cnt);
-    scan_buckets(cnt, excl, tot, wave_tot);
+    scan_buckets<M>(cnt, excl, tot, wave_tot);
     if (nchunks == 1) {
 #pragma unroll
-      for (int j = 0; j < kMaxMembers; ++j) total[j] = tot[j];
+      for (int j = 0; j < M; ++j) total[j] = tot[j];
     }
     // bucket j starts after every token of buckets < j
     int acc = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxMembers; ++j) {
+    for (int j = 0; j < M; ++j) {
       base[j] = acc;
       acc += total[j];
     }
     len = acc;
-    int pos[kMaxMembers];
+    int pos[M];
 #pragma unroll
-    for (int j = 0; j < kMaxMembers; ++j) pos[j] = base[j] + carry[j] + excl[j];
+    for (int j = 0; j < M; ++j) pos[j] = base[j] + carry[j] + excl[j];
     for (int w = w0; w < w1; ++w) {
-      uint32_t b[kMaxMembers];
+      uint32_t b[M];
 #pragma unroll
-      for (int j = 0; j < kMaxMembers; ++j) b[j] = j < members ? planes[j * W + w] : 0u;
+      for (int j = 0; j < M; ++j) b[j] = j < members ? planes[j * W + w] : 0u;
       uint32_t seen = 0u;
 #pragma unroll
-      for (int j = 0; j < kMaxMembers; ++j) {
+      for (int j = 0; j < M; ++j) {
         uint32_t fresh = b[j] & ~seen;
         seen |= b[j];
         while (fresh) {
@@ -387,7 +399,7 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuild
           fresh &= fresh - 1u;
           uint32_t own = 0u;
 #pragma unroll
-          for (int jj = 0; jj < kMaxMembers; ++jj) own |= ((b[jj] >> bit) & 1u) << jj;
+          for (int jj = 0; jj < M; ++jj) own |= ((b[jj] >> bit) & 1u) << jj;
           uidx[pos[j]] = c0 + w * 32 + bit;
           ubits[pos[j]] = (uint8_t)own;
           ++pos[j];
@@ -395,7 +407,7 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuild
       }
     }
 #pragma unroll
-    for (int j = 0; j < kMaxMembers; ++j) carry[j] += tot[j];
+    for (int j = 0; j < M; ++j) carry[j] += tot[j];
     __syncthreads();   // the planes are cleared for the next chunk
   }
   const int64_t width = (int64_t)p.G * p.topk;
@@ -456,8 +468,16 @@ hipError_t launch_union_build(const UnionBuildParams& p, hipStream_t stream) {
   if (p.G <= kMaxMembers && (size_t)p.G * words * sizeof(uint32_t) <= (size_t)kMergeLdsMax) {
     UnionBuildParams q = p;
     q.plane_words = (int32_t)(words > 0 ? words : 1);   // one chunk
-    hipLaunchKernelGGL(union_bitmap_kernel<false>, dim3(groups), dim3(kBitmapThreads),
-                       (size_t)p.G * q.plane_words * sizeof(uint32_t), stream, q);
+    const size_t lds = (size_t)p.G * q.plane_words * sizeof(uint32_t);
+    if (p.G <= 2)
+      hipLaunchKernelGGL((union_bitmap_kernel<false, 2>), dim3(groups), dim3(kBitmapThreads), lds,
+                         stream, q);
+    else if (p.G <= 4)
+      hipLaunchKernelGGL((union_bitmap_kernel<false, 4>), dim3(groups), dim3(kBitmapThreads), lds,
+                         stream, q);
+    else
+      hipLaunchKernelGGL((union_bitmap_kernel<false, kMaxMembers>), dim3(groups),
+                         dim3(kBitmapThreads), lds, stream, q);
     return hipGetLastError();
   }
   switch (p.topk_pad) {
@@ -488,8 +508,14 @@ hipError_t launch_union_build_ragged(UnionBuildParams p, int32_t* gstart, hipStr
   // 16 KB of planes (65536 tokens per chunk at G = 2): small enough for
   // several workgroups per CU; longer contexts take more chunks
   p.plane_words = (int32_t)(kRaggedPlaneBytes / (int)sizeof(uint32_t) / p.G);
-  hipLaunchKernelGGL(union_bitmap_kernel<true>, dim3((unsigned)p.num_groups), dim3(kBitmapThreads),
-                     (size_t)p.G * p.plane_words * sizeof(uint32_t), stream, p);
+  const size_t lds = (size_t)p.G * p.plane_words * sizeof(uint32_t);
+  const dim3 grid((unsigned)p.num_groups), block(kBitmapThreads);
+  if (p.G <= 2)
+    hipLaunchKernelGGL((union_bitmap_kernel<true, 2>), grid, block, lds, stream, p);
+  else if (p.G <= 4)
+    hipLaunchKernelGGL((union_bitmap_kernel<true, 4>), grid, block, lds, stream, p);
+  else
+    hipLaunchKernelGGL((union_bitmap_kernel<true, kMaxMembers>), grid, block, lds, stream, p);
   return hipGetLastError();
 }
 
