@@ -129,6 +129,19 @@ def test_entry_points_reject_without_touching_device():
                                    None) == -1
 
 
+def test_grid_beyond_one_launch_is_refused_on_the_host():
+    # 2^31 - 1 rows over 16 KV heads (group 1, four rows per one-wave team)
+    # need 2^33 teams: refused before any launch, not wrapped to a small grid
+    lib = sa.lib()
+    d = _desc(num_q_heads=16, num_kv_heads=16, q_row_stride=16 * 256, kv_row_stride=16 * 256,
+              v_row_stride=16 * 256, out_row_stride=16 * 256)
+    before = sa.sa_call_count("sparse_attn_prefill")
+    st = lib.sparse_attn_prefill(ctypes.byref(d), 0x1000, 0x2000, 0x3000, 0x4000, None,
+                                 (1 << 31) - 1, 10, 0x5000, 0x6000, None)
+    assert st == -2 and "exceed one launch" in sa.sa_last_error()
+    assert sa.sa_call_count("sparse_attn_prefill") == before
+
+
 def test_bad_entry_count_is_zero():
     assert sa.sa_call_count(99) == 0
     assert sa.sa_call_count(-1) == 0

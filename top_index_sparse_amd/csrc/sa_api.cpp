@@ -148,6 +148,10 @@ sa_status launch_attention(Kernel kernel, const sa::AttnParams& p, int union_mod
     default:
       return fail(SA_ERR_UNSUPPORTED, "no kernel for this head-dim combination");
   }
+  // the launchers refuse a grid beyond one launch before calling HIP
+  if (e == hipErrorInvalidConfiguration)
+    return fail(SA_ERR_SHAPE, "%d rows x %d KV heads exceed one launch", p.num_rows,
+                p.num_kv_heads);
   if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return SA_OK;
 }
@@ -277,8 +281,6 @@ sa_status sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const voi
   if (num_rows == 0) return ok(SA_ENTRY_PREFILL);
   st = check_ptrs(desc, q, k, v, idx, out, lse);
   if (st != SA_OK) return st;
-  if ((int64_t)(num_rows + 3) / 4 * desc->num_kv_heads > INT32_MAX)
-    return fail(SA_ERR_SHAPE, "too many rows for one launch");
   sa::AttnParams p = make_params(desc, q, k, v, idx, out, lse, num_rows);
   p.topk_len = topk_len;
   p.kv_len = kv_len;
@@ -539,6 +541,8 @@ sa_status sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_page_desc*
   c.splits = L.splits;
   c.num_q_heads = desc->num_q_heads;
   const hipError_t e = sa::launch_decode_mla576_fp8(p, c, stream);
+  if (e == hipErrorInvalidConfiguration)
+    return fail(SA_ERR_SHAPE, "decode of batch %d does not fit one launch", batch);
   if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok(SA_ENTRY_DECODE_PAGED);
 }

@@ -660,19 +660,19 @@ attn_kernel(AttnParams p) {
     attn_team<DQK, DV, V_IN_K, MODE, C, WSPLIT, FP8>(p, bid, w, xch, klds, qtok, qbits);
 }
 
-// Workgroups and threads per workgroup for a launch.
+// Workgroups and threads per workgroup for a launch; false when one launch
+// cannot hold them (at most 2^32 - 1 threads along x).
 template <int WSPLIT>
-inline void attn_grid(const AttnParams& p, int mode, dim3* grid, dim3* block) {
+inline bool attn_grid(const AttnParams& p, int mode, dim3* grid, dim3* block) {
   const int64_t teams =
       mode == kUnion ? (int64_t)p.num_groups * p.teams_per_group * p.num_kv_heads
-                     : (int64_t)((p.num_rows + p.rows_per_team - 1) / p.rows_per_team) * p.num_kv_heads;
-  if (WSPLIT == 1) {
-    *grid = dim3((unsigned)((teams + 3) / 4));
-    *block = dim3(256);
-  } else {
-    *grid = dim3((unsigned)teams);
-    *block = dim3(64 * WSPLIT);
-  }
+                     : ((int64_t)p.num_rows + p.rows_per_team - 1) / p.rows_per_team * p.num_kv_heads;
+  const int64_t blocks = WSPLIT == 1 ? (teams + 3) / 4 : teams;
+  const int64_t threads = WSPLIT == 1 ? 256 : 64 * WSPLIT;
+  if (blocks * threads > (int64_t)UINT32_MAX) return false;
+  *grid = dim3((unsigned)blocks);
+  *block = dim3((unsigned)threads);
+  return true;
 }
 
 }  // namespace sa

@@ -116,12 +116,15 @@ hipError_t launch_decode_mla576_fp8(AttnParams p, const DecodeCombineParams& c,
                                     hipStream_t stream) {
   p.rows_per_team = 1;
   dim3 grid, block;
-  attn_grid<2>(p, kRows, &grid, &block);   // one team per (request, range)
+  if (!attn_grid<2>(p, kRows, &grid, &block)) return hipErrorInvalidConfiguration;
+  // one team per (request, range)
   hipLaunchKernelGGL((attn_kernel<576, 512, true, kDecode, 1, 2, true, 2>), grid, block, 0, stream,
                      p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(c.batch * c.num_q_heads)),
+  const int64_t blocks = (int64_t)c.batch * c.num_q_heads;
+  if (blocks * kCombineThreads > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)blocks),
                      dim3(kCombineThreads), 0, stream, c);
   return hipGetLastError();
 }

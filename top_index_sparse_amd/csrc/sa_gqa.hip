@@ -8,22 +8,20 @@ namespace sa {
 namespace {
 
 template <int MODE, int C, int WSPLIT>
-void launch(const AttnParams& p, hipStream_t stream) {
+hipError_t launch(const AttnParams& p, hipStream_t stream) {
   dim3 grid, block;
-  attn_grid<WSPLIT>(p, MODE, &grid, &block);
+  if (!attn_grid<WSPLIT>(p, MODE, &grid, &block)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((attn_kernel<256, 256, false, MODE, C, WSPLIT, false, 2>), grid, block, 0, stream, p);
+  return hipGetLastError();
 }
 
 // One wave with whole K/V rows for 16 columns; two waves, each with half of
 // d, for 32 or 48 columns (union teams have at most 32).
 template <int MODE>
-void launch_cols(const AttnParams& p, int cols, hipStream_t stream) {
-  if (cols <= 16)
-    launch<MODE, 1, 1>(p, stream);
-  else if (MODE == kUnion || cols <= 32)
-    launch<MODE, 2, 2>(p, stream);
-  else
-    launch<kRows, 3, 2>(p, stream);
+hipError_t launch_cols(const AttnParams& p, int cols, hipStream_t stream) {
+  if (cols <= 16) return launch<MODE, 1, 1>(p, stream);
+  if (MODE == kUnion || cols <= 32) return launch<MODE, 2, 2>(p, stream);
+  return launch<kRows, 3, 2>(p, stream);
 }
 
 }  // namespace
@@ -37,13 +35,11 @@ hipError_t launch_attn_gqa256(AttnParams p, int union_mode, hipStream_t stream) 
   if (union_mode) {
     p.rows_per_team = p.G;
     p.teams_per_group = 1;
-    launch_cols<kUnion>(p, p.G * p.group, stream);
-  } else {
-    const int r = p.group <= 8 ? 16 / p.group : 48 / p.group;
-    p.rows_per_team = r < 4 ? r : 4;
-    launch_cols<kRows>(p, p.rows_per_team * p.group, stream);
+    return launch_cols<kUnion>(p, p.G * p.group, stream);
   }
-  return hipGetLastError();
+  const int r = p.group <= 8 ? 16 / p.group : 48 / p.group;
+  p.rows_per_team = r < 4 ? r : 4;
+  return launch_cols<kRows>(p, p.rows_per_team * p.group, stream);
 }
 
 }  // namespace sa

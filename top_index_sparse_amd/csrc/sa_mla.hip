@@ -10,32 +10,31 @@ namespace sa {
 namespace {
 
 template <bool FP8>
-void launch(AttnParams p, int union_mode, hipStream_t stream) {
+hipError_t launch(AttnParams p, int union_mode, hipStream_t stream) {
   dim3 grid, block;
   const int r = 16 / p.group;   // rows of one 16-column tile
   if (union_mode) {
     p.rows_per_team = r < p.G ? r : p.G;
     p.teams_per_group = (p.G + p.rows_per_team - 1) / p.rows_per_team;
-    attn_grid<2>(p, kUnion, &grid, &block);
+    if (!attn_grid<2>(p, kUnion, &grid, &block)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((attn_kernel<576, 512, true, kUnion, 1, 2, FP8, 2>), grid, block, 0, stream, p);
   } else {
     p.rows_per_team = r < 4 ? r : 4;
-    attn_grid<2>(p, kRows, &grid, &block);
+    if (!attn_grid<2>(p, kRows, &grid, &block)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((attn_kernel<576, 512, true, kRows, 1, 2, FP8, 2>), grid, block, 0, stream, p);
   }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_mla576(AttnParams p, int union_mode, hipStream_t stream) {
-  launch<false>(p, union_mode, stream);
-  return hipGetLastError();
+  return launch<false>(p, union_mode, stream);
 }
 
 // K rows as 656-byte FP8 records, dequantised while they are staged.
 hipError_t launch_attn_mla576_fp8(AttnParams p, int union_mode, hipStream_t stream) {
-  launch<true>(p, union_mode, stream);
-  return hipGetLastError();
+  return launch<true>(p, union_mode, stream);
 }
 
 }  // namespace sa
