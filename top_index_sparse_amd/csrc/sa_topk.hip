@@ -4,16 +4,16 @@
 // equal scores going to the lower position, and writes the kept positions in
 // ascending order; a row with n_t <= k writes 0 .. n_t - 1 and pads with -1.
 //
-// gfx950 design: one 1024-thread workgroup per row.
+// gfx950 design: one 1024-thread workgroup per row, two resident per CU.
 //   Keys. A score's bits map to a uint32 key whose unsigned order is the
 //   float order (-0 is folded onto +0 first, so the two tie).
 //   Level 0. An LDS histogram of the keys' top 13 bits (8192 bins, wide
 //   enough that scores crowding a few exponents still spread their atomics)
 //   and a block-wide scan from the top bin down find the bin b0 that holds
 //   the k-th largest key.
-//   Classes. Every element is then above b0 (kept), in b0 (a candidate) or
-//   below (dropped), recorded in two LDS bitmaps by position. Candidates,
-//   usually a few hundred, are compacted into a list in position order;
+//   Classes. Every element is then above b0 (kept, into an LDS bitmap by
+//   position), in b0 (a candidate) or below (dropped). Candidates, usually a
+//   few hundred, are appended to an LDS list straight from the registers;
 //   levels 1 and 2 (11 and 8 more bits) run on that list alone and mark each
 //   candidate kept or tied in two more bitmaps.
 //   Output. Thread j owns bitmap words (positions 32 words at a time, in
@@ -23,12 +23,14 @@
 //   to (kept before it) + min(tied before it, still needed), and a tie is
 //   kept while fewer than that many ties precede it.
 //   Rows of up to 32768 positions keep their keys in registers from the
-//   single read to the classes; rows up to 65536 read the scores twice.
-//   When the candidates overflow their list (scores crowding one bin),
-//   levels 1 and 2 and the marking read the row again instead. Longer rows
-//   take a generic kernel that runs every level over the row, reads it again
-//   for each pass, and orders the output with per-wave ballots and a scan of
-//   (chunk, wave) totals.
+//   single read to the classes; rows up to 65536 read the scores twice. A
+//   read issues all of its chunks (or a group of them) before it converts
+//   the first to keys, so the chunks' loads are in flight together. When the candidates overflow their list
+//   (scores crowding one bin), levels 1 and 2 and the marking read the row
+//   again instead. Longer rows take a generic kernel, one workgroup per row,
+//   that runs every level over the row, reads it again for each pass, and
+//   orders the output with per-wave ballots and a scan of (chunk, wave)
+//   totals.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -58,29 +60,43 @@ struct TopkLds {
   uint32_t wtie[kBatch * kWaves + 1];
 };
 
+// Inclusive prefix sums within each row of 16 lanes (DPP row shifts; lanes
+// shifted in from outside the row add 0).
+__device__ __forceinline__ uint32_t row_scan16(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  return x;
+}
+
+// Inclusive prefix sums over the wave's 64 lanes: the rows' own scans, then
+// row_bcast:15 adds row 0's total to row 1 and row 2's to row 3, and
+// row_bcast:31 adds the total of rows 0-1 to rows 2 and 3 (the other rows
+// are masked off and add 0).
+__device__ __forceinline__ uint32_t wave_scan64(uint32_t x) {
+  x = row_scan16(x);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);
+  return x;
+}
+
+static_assert(kWaves == 16, "the per-wave totals are scanned as one row of 16 lanes");
+
 // Exclusive prefix over the block of one value per thread; *total gets the
 // block's sum. Two barriers.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* red,
+__device__ __forceinline__ uint32_t block_exclusive_scan(int tid, uint32_t v, uint32_t* red,
                                                          uint32_t* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t x = wave_scan64(v);
   if (lane == 63) red[wv] = x;
   __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t s = red[w];
-    before += w < wv ? s : 0u;
-    all += s;
-  }
+  const uint32_t r = row_scan16(red[lane & 15]);   // lane w: waves 0..w
   __syncthreads();
-  *total = all;
-  return before + x - v;
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)r, kWaves - 1);
+  const uint32_t before = (uint32_t)__builtin_amdgcn_readlane((int)r, wv > 0 ? wv - 1 : 0);
+  return (wv > 0 ? before : 0u) + x - v;
 }
 
 // Prefix over the wave's lanes below this one, and the wave's total, of a
@@ -101,15 +117,14 @@ __device__ __forceinline__ void wave_prefix3(uint32_t v, uint32_t* before, uint3
 // After a histogram of nb bins: the bin holding the need-th largest counted
 // key (scanning from the top bin down) and how many of that bin are still
 // needed. *whole: the bin is needed entirely. Ends with hist reusable.
-__device__ __forceinline__ void find_bin(TopkLds& L, int nb, uint32_t* need, uint32_t* bin,
+__device__ __forceinline__ void find_bin(TopkLds& L, int tid, int nb, uint32_t* need, uint32_t* bin,
                                          bool* whole) {
-  const int tid = threadIdx.x;
   const int per = nb >= kThreads ? nb / kThreads : 1;
   const int top = nb - 1 - per * tid;
   uint32_t mine = 0;
   for (int j = 0; j < per; ++j) mine += top - j >= 0 ? L.hist[top - j] : 0u;
   uint32_t tot;
-  uint32_t above = block_exclusive_scan(mine, L.red, &tot);
+  uint32_t above = block_exclusive_scan(tid, mine, L.red, &tot);
   if (above < *need && *need <= above + mine) {
     for (int j = 0; j < per; ++j) {
       const uint32_t h = L.hist[top - j];
@@ -200,24 +215,62 @@ __device__ __forceinline__ void write_output(TopkLds& L, int nchunks, uint32_t n
   }
 }
 
-__device__ __forceinline__ void load4_keys(const float* row, int n, bool vec, int i,
-                                           uint32_t k4[4]) {
-  const int pos = 4 * (i * kThreads + (int)threadIdx.x);
-  if (vec && pos + 3 < n) {
-    const float4 v = *reinterpret_cast<const float4*>(row + pos);
-    k4[0] = score_key(__float_as_uint(v.x));
-    k4[1] = score_key(__float_as_uint(v.y));
-    k4[2] = score_key(__float_as_uint(v.z));
-    k4[3] = score_key(__float_as_uint(v.w));
-  } else {
+// The raw score bits of this thread's positions 4 (i kThreads + tid) .. +3
+// of chunk i. Loads only, and no use of their values, so that the loads of
+// several chunks are all in flight before the first wait (a key computed
+// inside the branch would make each load wait for itself). vlen: how many
+// positions from the row's start may be read with 16-byte loads (the row's
+// storage, kv_len, when the row is 16-byte aligned; else 0). A chunk inside
+// that span is read with one 16-byte load per thread, the thread whose four
+// positions straddle n included (keys4 masks what lies past n); other
+// chunks read one score at a time, positions past n reading the row's last
+// score. Positions of threads wholly past n get 0xffffffff, whose key is 0.
+__device__ __forceinline__ void load4_raw(int tid, const float* row, int n, int vlen, int i,
+                                          uint32_t r[4]) {
+  const int base = 4 * i * kThreads;
+  const int pos = base + 4 * tid;
+  // (two independent uniform tests rather than if / else: at an if / else
+  // join the compiler may give one side's load addresses the registers the
+  // other side loads into, and then waits for older loads in flight)
+  const bool wide = base < n && base + 4 * kThreads <= vlen;
+  const bool narrow = !wide && base < n;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) k4[c] = pos + c < n ? score_key(__float_as_uint(row[pos + c])) : 0u;
+  for (int c = 0; c < 4; ++c) r[c] = 0xffffffffu;
+  if (wide && pos < n) {
+    const float4 v = *reinterpret_cast<const float4*>(row + pos);
+    r[0] = __float_as_uint(v.x);
+    r[1] = __float_as_uint(v.y);
+    r[2] = __float_as_uint(v.z);
+    r[3] = __float_as_uint(v.w);
   }
+  if (narrow) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r[c] = __float_as_uint(row[pos + c < n ? pos + c : n - 1]);
+  }
+}
+
+// Keys of chunk i's positions from their raw bits, in place; 0 past the row
+// (no score maps to 0).
+__device__ __forceinline__ void keys4(int tid, int n, int i, uint32_t k4[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) k4[c] = score_key(k4[c]);
+  const int base = 4 * i * kThreads;
+  if (base < n && base + 4 * kThreads > n) {   // the chunk straddles the row's end (uniform)
+    const int pos = base + 4 * tid;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) k4[c] = pos + c < n ? k4[c] : 0u;
+  }
+}
+
+__device__ __forceinline__ void load4_keys(int tid, const float* row, int n, int vlen, int i,
+                                           uint32_t k4[4]) {
+  load4_raw(tid, row, n, vlen, i, k4);
+  keys4(tid, n, i, k4);
 }
 
 // Generic path, any row length: every level and the output re-read the
 // row's scores (0 keys = past the row; no score maps to 0).
-__device__ __forceinline__ void select_generic(TopkLds& L, const float* row, int n, bool vec, int k,
+__device__ __forceinline__ void select_generic(TopkLds& L, const float* row, int n, int vlen, int k,
                                int32_t* out) {
   const int tid = threadIdx.x;
   const int nchunks = (n + 4 * kThreads - 1) / (4 * kThreads);
@@ -233,7 +286,7 @@ __device__ __forceinline__ void select_generic(TopkLds& L, const float* row, int
     __syncthreads();
     for (int i = 0; i < nchunks; ++i) {
       uint32_t k4[4];
-      load4_keys(row, n, vec, i, k4);
+      load4_keys(tid, row, n, vlen, i, k4);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const uint32_t kk = k4[c];
@@ -244,14 +297,14 @@ __device__ __forceinline__ void select_generic(TopkLds& L, const float* row, int
     __syncthreads();
     uint32_t bin;
     bool whole;
-    find_bin(L, nb, &need, &bin, &whole);
+    find_bin(L, tid, nb, &need, &bin, &whole);
     prefix = (shift == 32 ? 0u : prefix << bits) | bin;
     shift = sh;
     if (whole) break;
   }
   write_output(L, nchunks, need, k, out, [&](int i, uint32_t* fs, uint32_t* ft) {
     uint32_t k4[4];
-    load4_keys(row, n, vec, i, k4);
+    load4_keys(tid, row, n, vlen, i, k4);
     uint32_t s = 0, t = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -266,52 +319,41 @@ __device__ __forceinline__ void select_generic(TopkLds& L, const float* row, int
 
 // Exclusive prefixes over the block of two values per thread; *t1, *t2
 // get the block's sums. Two barriers; red holds 2 * kWaves words.
-__device__ __forceinline__ void block_exclusive_scan2(uint32_t v1, uint32_t v2, uint32_t* red,
+__device__ __forceinline__ void block_exclusive_scan2(int tid, uint32_t v1, uint32_t v2,
+                                                      uint32_t* red,
                                                       uint32_t* e1, uint32_t* e2, uint32_t* t1,
                                                       uint32_t* t2) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint32_t x1 = v1, x2 = v2;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y1 = __shfl_up(x1, o), y2 = __shfl_up(x2, o);
-    if (lane >= o) {
-      x1 += y1;
-      x2 += y2;
-    }
-  }
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t x1 = wave_scan64(v1), x2 = wave_scan64(v2);
   if (lane == 63) {
     red[wv] = x1;
     red[kWaves + wv] = x2;
   }
   __syncthreads();
-  uint32_t b1 = 0, b2 = 0, a1 = 0, a2 = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t s1 = red[w], s2 = red[kWaves + w];
-    b1 += w < wv ? s1 : 0u;
-    b2 += w < wv ? s2 : 0u;
-    a1 += s1;
-    a2 += s2;
-  }
+  const uint32_t r1 = row_scan16(red[lane & 15]), r2 = row_scan16(red[kWaves + (lane & 15)]);
   __syncthreads();
-  *e1 = b1 + x1 - v1;
-  *e2 = b2 + x2 - v2;
-  *t1 = a1;
-  *t2 = a2;
+  const int prev = wv > 0 ? wv - 1 : 0;
+  const uint32_t b1 = (uint32_t)__builtin_amdgcn_readlane((int)r1, prev);
+  const uint32_t b2 = (uint32_t)__builtin_amdgcn_readlane((int)r2, prev);
+  *e1 = (wv > 0 ? b1 : 0u) + x1 - v1;
+  *e2 = (wv > 0 ? b2 : 0u) + x2 - v2;
+  *t1 = (uint32_t)__builtin_amdgcn_readlane((int)r1, kWaves - 1);
+  *t2 = (uint32_t)__builtin_amdgcn_readlane((int)r2, kWaves - 1);
 }
 
 // Fast path for rows of at most kThreads * PER positions. Position bitmaps
 // in LDS (bit j of word w = position 32 w + j): kept by level 0 (above the
-// threshold bin, or all of a bin needed whole), candidates (in that bin),
-// and the candidates kept or tied after levels 1 and 2.
+// threshold bin, or all of a bin needed whole), and the candidates (keys in
+// that bin) kept or tied after levels 1 and 2.
 template <int PER>
 struct FastLds : TopkLds {
   static constexpr int kWords = PER * kThreads / 32;
   uint32_t amap[kWords];
-  uint32_t cmap[kWords];
   uint32_t selb[kWords];
   uint32_t tieb[kWords];
   uint32_t red2[2 * kWaves];
+  uint32_t ncand;
   uint32_t ckey[kCand];
   int32_t cpos[kCand];
 };
@@ -326,15 +368,20 @@ __device__ __forceinline__ int row_length(const TopkParams& p, int t) {
   return n;
 }
 
-// REG: the keys stay in registers from the single read to the classes.
+// One workgroup per row. REG: the row's scores are read once into
+// registers, all chunks requested before the first is used.
 template <int PER, bool REG>
 __global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
   __shared__ FastLds<PER> L;
   constexpr int NCH = PER / 4;                      // 4096-position chunks
+  // chunks per group: re-read groups are loaded whole before their first use
+  constexpr int GCH = REG ? (NCH < 8 ? NCH : 8) : 4;
+  static_assert(NCH % GCH == 0, "whole groups");
+  constexpr int GUNROLL = REG ? NCH / GCH : 1;   // re-read groups stay a loop
   constexpr int NWORDS = FastLds<PER>::kWords;      // bitmap words
   constexpr int WPT = NWORDS >= kThreads ? NWORDS / kThreads : 1;   // words per owner
   const int t = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int n = row_length(p, t);
   int32_t* out = p.idx + (int64_t)t * p.idx_row_stride;
   if (n <= p.k) {   // every visible position, then padding
@@ -342,33 +389,48 @@ __global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
     return;
   }
   const float* row = p.scores + (int64_t)t * p.score_row_stride;
-  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;   // 16-byte loads
-
-  // ---- level 0 --------------------------------------------------------------
-  for (int b = tid; b < kBins; b += kThreads) L.hist[b] = 0u;
-  for (int w = tid; w < NWORDS; w += kThreads) L.amap[w] = L.cmap[w] = L.selb[w] = L.tieb[w] = 0u;
+  // 16-byte loads over the row's storage when the row is aligned for them
+  const int vlen = (reinterpret_cast<uintptr_t>(row) & 15u) == 0 ? p.kv_len : 0;
   uint32_t kreg[REG ? PER : 1];
   if constexpr (REG) {
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) load4_keys(row, n, vec, i, &kreg[4 * i]);
+    for (int i = 0; i < NCH; ++i) load4_raw(tid, row, n, vlen, i, &kreg[4 * i]);
   }
-  auto keys = [&](int i, uint32_t k4[4]) {
-    if constexpr (REG) {
+  // chunk group g's keys: REG, from the registers; else read now, the
+  // group's chunks issued before their first use
+  uint32_t kg[REG ? 1 : 4 * GCH];
+  auto group_keys = [&](int g) {
+    if constexpr (!REG) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) k4[c] = kreg[4 * i + c];
-    } else {
-      load4_keys(row, n, vec, i, k4);
+      for (int i8 = 0; i8 < GCH; ++i8) load4_raw(tid, row, n, vlen, GCH * g + i8, &kg[4 * i8]);
+#pragma unroll
+      for (int i8 = 0; i8 < GCH; ++i8) keys4(tid, n, GCH * g + i8, &kg[4 * i8]);
     }
   };
+  auto keys = [&](int i, uint32_t k4[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) k4[c] = REG ? kreg[4 * i + c] : kg[4 * (i % GCH) + c];
+  };
+  uint32_t need = (uint32_t)p.k, b0 = 0;
+  bool whole0 = true;
+
+  // ---- level 0 --------------------------------------------------------------
+  for (int b = tid; b < kBins; b += kThreads) L.hist[b] = 0u;
+  for (int w = tid; w < NWORDS; w += kThreads) L.amap[w] = L.selb[w] = L.tieb[w] = 0u;
+  if (tid == 0) L.ncand = 0u;
+  if constexpr (REG) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) keys4(tid, n, i, &kreg[4 * i]);
+  }
   __syncthreads();
-  // chunks in groups of 8; re-read groups are kept apart so that at most 8
-  // chunks of loads are in flight. Past-the-row keys (0) are not counted:
-  // one bin taking thousands of same-address atomics would serialise them.
+  // Past-the-row keys (0) are not counted: one bin taking thousands of
+  // same-address atomics would serialise them.
+#pragma unroll GUNROLL
+  for (int g = 0; g < NCH / GCH; ++g) {
+    group_keys(g);
 #pragma unroll
-  for (int g = 0; g < (NCH + 7) / 8; ++g) {
-#pragma unroll
-    for (int i8 = 0; i8 < (NCH < 8 ? NCH : 8); ++i8) {
-      const int i = 8 * g + i8;
+    for (int i8 = 0; i8 < GCH; ++i8) {
+      const int i = GCH * g + i8;
       uint32_t k4[4];
       keys(i, k4);
       if ((i + 1) * 4 * kThreads <= n) {   // the whole chunk is inside the row
@@ -383,18 +445,19 @@ __global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
     if (!REG) __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
-  uint32_t need = (uint32_t)p.k, b0;
-  bool whole0;
-  find_bin(L, kBins, &need, &b0, &whole0);
+  find_bin(L, tid, kBins, &need, &b0, &whole0);
 
-  // ---- classes into the position bitmaps -------------------------------------
+  // ---- classes: kept into the bitmap, candidates into a list ----------------
   // chunk i covers positions 4 (i kThreads + tid) .. +3: one nibble of word
-  // (i kThreads + tid) / 8, shared with the 7 neighbouring threads
+  // (i kThreads + tid) / 8, shared with the 7 neighbouring threads. A
+  // wave appends its candidates of a chunk with one LDS atomic; the list
+  // is unordered (levels 1 and 2 count, the marks go by position).
+#pragma unroll GUNROLL
+  for (int g = 0; g < NCH / GCH; ++g) {
+    group_keys(g);
 #pragma unroll
-  for (int g = 0; g < (NCH + 7) / 8; ++g) {
-#pragma unroll
-    for (int i8 = 0; i8 < (NCH < 8 ? NCH : 8); ++i8) {
-      const int i = 8 * g + i8;
+    for (int i8 = 0; i8 < GCH; ++i8) {
+      const int i = GCH * g + i8;
       uint32_t k4[4];
       keys(i, k4);
       uint32_t a = 0, cm = 0;
@@ -404,43 +467,35 @@ __global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
         a |= (uint32_t)(d > b0 || (whole0 && d == b0)) << c;
         cm |= (uint32_t)(!whole0 && d == b0) << c;
       }
-      const int word = (i * kThreads + tid) >> 3;
-      const uint32_t sh = 4u * (uint32_t)(tid & 7);
-      if (a) atomicOr(&L.amap[word], a << sh);
-      if (cm) atomicOr(&L.cmap[word], cm << sh);
+      const int pos0 = 4 * (i * kThreads + tid);
+      if (a) atomicOr(&L.amap[pos0 >> 5], a << (pos0 & 31));
+      uint32_t before, total;
+      wave_prefix3((uint32_t)__popc(cm), &before, &total);
+      if (total) {   // wave-uniform
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&L.ncand, total);
+        uint32_t at = (uint32_t)__builtin_amdgcn_readlane((int)base, 0) + before;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if ((cm >> c) & 1u) {
+            if (at < (uint32_t)kCand) {
+              L.ckey[at] = k4[c];
+              L.cpos[at] = pos0 + c;
+            }
+            ++at;
+          }
+        }
+      }
     }
     if (!REG) __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
 
-  // ---- levels 1 and 2 on the candidates (or, on overflow, the row) -----------
+  // ---- levels 1 and 2 on the candidates (or, on overflow, the row) ---------
   uint32_t tie_need = 0;
   if (!whole0) {
-    // candidate list, compacted in position order by the bitmap words' owners
-    uint32_t mine = 0;
-#pragma unroll
-    for (int j = 0; j < WPT; ++j) {
-      const int w = tid * WPT + j;
-      mine += w < NWORDS ? __popc(L.cmap[w]) : 0u;
-    }
-    uint32_t nc;
-    uint32_t off = block_exclusive_scan(mine, L.red, &nc);
+    const uint32_t nc = L.ncand;
     const bool spill = nc > (uint32_t)kCand;   // candidates overflow their list
-    if (!spill && mine) {
-#pragma unroll
-      for (int j = 0; j < WPT; ++j) {
-        const int w = tid * WPT + j;
-        uint32_t m = w < NWORDS ? L.cmap[w] : 0u;
-        while (m) {
-          const int pos = 32 * w + __builtin_ctz(m);
-          m &= m - 1u;
-          L.ckey[off] = score_key(__float_as_uint(row[pos]));
-          L.cpos[off] = pos;
-          ++off;
-        }
-      }
-    }
-    __syncthreads();
     uint32_t prefix = b0;
     int shift = 19;
 #pragma unroll 1
@@ -459,7 +514,7 @@ __global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
 #pragma unroll 1
         for (int i = 0; i < NCH; ++i) {
           uint32_t k4[4];
-          load4_keys(row, n, vec, i, k4);
+          load4_keys(tid, row, n, vlen, i, k4);
 #pragma unroll
           for (int c = 0; c < 4; ++c)
             if (k4[c] != 0u && (k4[c] >> shift) == prefix)
@@ -469,7 +524,7 @@ __global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
       __syncthreads();
       uint32_t bin;
       bool whole;
-      find_bin(L, nb, &need, &bin, &whole);
+      find_bin(L, tid, nb, &need, &bin, &whole);
       prefix = (prefix << bits) | bin;
       shift = sh;
       if (whole) break;
@@ -486,7 +541,7 @@ __global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
 #pragma unroll 1
       for (int i = 0; i < NCH; ++i) {
         uint32_t k4[4];
-        load4_keys(row, n, vec, i, k4);
+        load4_keys(tid, row, n, vlen, i, k4);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
           if (k4[c] != 0u && (k4[c] >> 19) == b0) mark(k4[c], 4 * (i * kThreads + tid) + c);
@@ -496,22 +551,20 @@ __global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
     __syncthreads();
   }
 
-  // ---- output from the bitmaps, in position order ------------------------------
+  // ---- output from the bitmaps, in position order ----------------------------
   // An element goes to (kept before it) + min(tied before it, tie_need); a
   // tie is kept while fewer than tie_need ties precede it.
   uint32_t ksel[WPT], ktie[WPT], ns = 0, nt = 0;
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
     const int w = tid * WPT + j;
-    const uint32_t am = w < NWORDS ? L.amap[w] : 0u;
-    const uint32_t cm = w < NWORDS ? L.cmap[w] : 0u;
-    ksel[j] = am | (cm & (w < NWORDS ? L.selb[w] : 0u));
-    ktie[j] = cm & (w < NWORDS ? L.tieb[w] : 0u);
+    ksel[j] = w < NWORDS ? (L.amap[w] | L.selb[w]) : 0u;
+    ktie[j] = w < NWORDS ? L.tieb[w] : 0u;
     ns += __popc(ksel[j]);
     nt += __popc(ktie[j]);
   }
   uint32_t kept, tied, ts, tt;
-  block_exclusive_scan2(ns, nt, L.red2, &kept, &tied, &ts, &tt);
+  block_exclusive_scan2(tid, ns, nt, L.red2, &kept, &tied, &ts, &tt);
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
     const int w = tid * WPT + j;
@@ -543,7 +596,8 @@ __global__ void __launch_bounds__(kThreads) topk_generic_kernel(TopkParams p) {
     return;
   }
   const float* row = p.scores + (int64_t)t * p.score_row_stride;
-  select_generic(L, row, n, (reinterpret_cast<uintptr_t>(row) & 15u) == 0, p.k, out);
+  select_generic(L, row, n, (reinterpret_cast<uintptr_t>(row) & 15u) == 0 ? p.kv_len : 0, p.k,
+                 out);
 }
 
 }  // namespace
