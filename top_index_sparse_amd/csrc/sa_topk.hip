@@ -81,6 +81,14 @@ __device__ __forceinline__ uint32_t wave_scan64(uint32_t x) {
   return x;
 }
 
+// OR of lanes 8j .. 8j+7 in lane 8j+7 (groups of 8 lie inside a DPP row).
+__device__ __forceinline__ uint32_t or8_into_top(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  return v;
+}
+
 static_assert(kWaves == 16, "the per-wave totals are scanned as one row of 16 lanes");
 
 // Exclusive prefix over the block of one value per thread; *total gets the
@@ -416,7 +424,7 @@ __global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
 
   // ---- level 0 --------------------------------------------------------------
   for (int b = tid; b < kBins; b += kThreads) L.hist[b] = 0u;
-  for (int w = tid; w < NWORDS; w += kThreads) L.amap[w] = L.selb[w] = L.tieb[w] = 0u;
+  for (int w = tid; w < NWORDS; w += kThreads) L.selb[w] = L.tieb[w] = 0u;   // (amap: below)
   if (tid == 0) L.ncand = 0u;
   if constexpr (REG) {
 #pragma unroll
@@ -449,12 +457,15 @@ __global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
 
   // ---- classes: kept into the bitmap, candidates into a list ----------------
   // chunk i covers positions 4 (i kThreads + tid) .. +3: one nibble of word
-  // (i kThreads + tid) / 8, shared with the 7 neighbouring threads. A
-  // wave appends its candidates of a chunk with one LDS atomic; the list
-  // is unordered (levels 1 and 2 count, the marks go by position).
+  // (i kThreads + tid) / 8, shared with the 7 neighbouring lanes; the eight
+  // nibbles are ORed across lanes and the top lane writes the word (every
+  // word once, so the bitmap needs no clearing). A chunk group's candidates
+  // are appended to the list with one wave scan and one LDS atomic per wave;
+  // the list is unordered (levels 1 and 2 count, the marks go by position).
 #pragma unroll GUNROLL
   for (int g = 0; g < NCH / GCH; ++g) {
     group_keys(g);
+    uint32_t cmask = 0;   // bit 4 i8 + c: candidate position c of chunk GCH g + i8
 #pragma unroll
     for (int i8 = 0; i8 < GCH; ++i8) {
       const int i = GCH * g + i8;
@@ -468,21 +479,39 @@ __global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
         cm |= (uint32_t)(!whole0 && d == b0) << c;
       }
       const int pos0 = 4 * (i * kThreads + tid);
-      if (a) atomicOr(&L.amap[pos0 >> 5], a << (pos0 & 31));
-      uint32_t before, total;
-      wave_prefix3((uint32_t)__popc(cm), &before, &total);
+      const uint32_t word = or8_into_top(a << (pos0 & 31));
+      if ((tid & 7) == 7) L.amap[pos0 >> 5] = word;
+      cmask |= cm << (4 * i8);
+      // (materialised per chunk: the compare masks would otherwise stay in
+      // scalar registers until the group ends, 64 of them for eight chunks,
+      // enough to keep a second workgroup off the CU)
+      __asm__ volatile("" : "+v"(cmask));
+    }
+    if (!whole0) {
+      const uint32_t cnt = (uint32_t)__popc(cmask);
+      const uint32_t incl = wave_scan64(cnt);
+      const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
       if (total) {   // wave-uniform
         uint32_t base = 0;
         if (lane == 0) base = atomicAdd(&L.ncand, total);
-        uint32_t at = (uint32_t)__builtin_amdgcn_readlane((int)base, 0) + before;
+        uint32_t at = (uint32_t)__builtin_amdgcn_readlane((int)base, 0) + incl - cnt;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if ((cm >> c) & 1u) {
-            if (at < (uint32_t)kCand) {
-              L.ckey[at] = k4[c];
-              L.cpos[at] = pos0 + c;
+        for (int i8 = 0; i8 < GCH; ++i8) {
+          const uint32_t nib = (cmask >> (4 * i8)) & 0xfu;
+          if (nib) {
+            const int i = GCH * g + i8;
+            uint32_t k4[4];
+            keys(i, k4);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              if ((nib >> c) & 1u) {
+                if (at < (uint32_t)kCand) {
+                  L.ckey[at] = k4[c];
+                  L.cpos[at] = 4 * (i * kThreads + tid) + c;
+                }
+                ++at;
+              }
             }
-            ++at;
           }
         }
       }
