@@ -365,22 +365,36 @@ def measure_others(args, sa, torch, stream):
         dout = torch.empty((B, Hq, 512), dtype=torch.float32, device="cuda")
         dlse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
 
-        def decode():
+        def decode(s=stream):
             sa.sparse_attn_decode_paged(dq, dst, didx, dst_page_tokens=c.dst_page_tokens,
                                         scale_bytes=c.scale_bytes, sm_scale=c.scale, ws=dws,
-                                        out=dout, lse=dlse, stream=stream)
+                                        out=dout, lse=dlse, stream=s)
 
-        def step():
-            sa.page_mark(didx, c.num_src_pages, c.src_page_tokens, mask=mask, stream=stream)
-            sa.page_split(src, dst, mask, **geom)
-            decode()
+        def step(s=stream):
+            sa.page_mark(didx, c.num_src_pages, c.src_page_tokens, mask=mask, stream=s)
+            sa.page_split(src, dst, mask, **{**geom, "stream": s})
+            decode(s)
 
         step()
         ms_dec = _events_ms(torch, stream, decode, w, n)
         ms_step = _events_ms(torch, stream, step, w, n)
+        # the same step (five kernel launches) captured once in a HIP graph
+        # and replayed: what a serving loop pays per step without the host's
+        # per-launch cost (the calls launch on the capture stream)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(None)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(None)
+        ms_graph = _events_ms(torch, stream, graph.replay, w, n)
         valid = int(((c.idx >= 0) & (c.idx < c.num_src_pages * c.src_page_tokens)).sum())
         r = _rate(valid * FP8_RECORD_BYTES, ms_dec)
-        r.update({"valid_slots": valid, "step_ms": round(ms_step, 4)})
+        r.update({"valid_slots": valid, "step_ms": round(ms_step, 4),
+                  "step_graph_ms": round(ms_graph, 4)})
         return r
 
     res["decode_attention"] = decode_lines(c, src, dst, didx, mask)
