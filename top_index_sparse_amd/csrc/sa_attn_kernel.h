@@ -59,8 +59,9 @@
 //   operands from there.
 //
 // Invalid slots (outside [0, kv_len), past topk or topk_len, or owned by
-// none of the team's rows) issue no memory traffic and are masked to -inf
-// before the softmax. Workgroups are remapped so that each XCD (own L2)
+// none of the team's rows) read a cache-resident 2 KB row of zeros and are
+// masked to -inf before the softmax; a tile with no valid slot for the team
+// is skipped whole. Workgroups are remapped so that each XCD (own L2)
 // works on bands of consecutive rows, which share most of their slots.
 #pragma once
 
@@ -116,6 +117,12 @@ struct AttnTile {
     u32x4_t vd[4 * VCH];   // vd[VCH*i + h]: slot 4g+i, d = 128h + 8m .. +7
   };
 };
+
+// What an invalid slot's lanes load instead of a K or V row: zeros, so the
+// loads need no branch (a load under a per-lane branch cannot be counted,
+// and waiting for any later load then waits for all of them) and an invalid
+// slot's V is exactly 0. Every row offset read here is below 2 KB.
+static __device__ __attribute__((aligned(16))) uint8_t kZeroRow[2048];
 
 // Team `team_id`, wavefront `split` of WSPLIT. xch: partial-score exchange
 // [2][WG_WAVES][C][64]; klds: per-wave K tiles; qtok/qbits: per-wave queues.
@@ -330,10 +337,8 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     return Tile{m0, (uint32_t)(bm >> (4 * slot_l)) & 0xfu};
   };
 
-  // Invalid slots skip their loads. Their K registers keep stale values
-  // (their scores are forced to -inf), and their V registers keep stale
-  // finite values from an earlier tile, or the zeros set before the loop,
-  // which are multiplied by p = 0.
+  // Invalid slots load the zero row (their scores are forced to -inf, and
+  // their V is 0, multiplied by p = 0).
   const uint32_t k_row_bytes = (uint32_t)(2 * p.k_row_stride);   // < 2^32 (host check)
   const uint32_t v_row_bytes = (uint32_t)(2 * p.v_row_stride);
   // FP8 records: kvh's record of row 0 (k_row_stride counts 2-byte units)
@@ -370,12 +375,11 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
       row_bcast4((int)koff, klo);
       const int ir = n >> 2, is = n & 3;
       auto pick = [](const int a[4], int i) { return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3]; };
+      auto rec = [&](int lo, int hi) { return hi >= 0 ? kwb + join64(lo, hi) : kZeroRow; };
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (khi[i] >= 0) td.kd[i] = ld16(kwb + join64(klo[i], khi[i]) + 256 * split + 16 * n);
-      const int rhi = pick(khi, ir), shi = pick(khi, is);
-      if (rhi >= 0) td.kd[4] = ld16(kwb + join64(pick(klo, ir), rhi) + 528 + 64 * split + 16 * is);
-      if (shi >= 0) td.kd[5] = ld16(kwb + join64(pick(klo, is), shi) + 512);
+      for (int i = 0; i < 4; ++i) td.kd[i] = ld16(rec(klo[i], khi[i]) + 256 * split + 16 * n);
+      td.kd[4] = ld16(rec(pick(klo, ir), pick(khi, ir)) + 528 + 64 * split + 16 * is);
+      td.kd[5] = ld16(rec(pick(klo, is), pick(khi, is)) + 512);
       return;
     }
     if constexpr (VKLDS) {
@@ -396,7 +400,7 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
         const int hi = nx ? khi[i0 < 3 ? i0 + 1 : 3] : khi[i0];
         const int ch = c - CPR * (nx ? i0 + 1 : i0);
         const int d = ch < MAIN / 8 ? split * MAIN + 8 * ch : DV + split * ROPE + 8 * (ch - MAIN / 8);
-        if (hi >= 0) td.kd[q] = ld16(kwb + join64(lo, hi) + 2 * d);
+        td.kd[q] = ld16((hi >= 0 ? kwb + join64(lo, hi) : kZeroRow) + 2 * d);
       }
       return;
     }
@@ -407,15 +411,14 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     row_bcast4((int)(voff >> 32), vhi);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (khi[i] >= 0) {
-        // K and V rows of slot 4g+i, bytes 256h + 16m: sixteen lanes per row
-        const uint8_t* kp = kbn + join64(klo[i], khi[i]);
+      // K and V rows of slot 4g+i, bytes 256h + 16m: sixteen lanes per row
+      const bool ok = khi[i] >= 0;
+      const uint8_t* kp = ok ? kbn + join64(klo[i], khi[i]) : kZeroRow + 16 * n;
+      const uint8_t* vp = ok ? vbn + join64(vlo[i], vhi[i]) : kZeroRow + 16 * n;
 #pragma unroll
-        for (int h = 0; h < KCH; ++h) td.kd[KCH * i + h] = ld16(kp + 256 * h);
-        const uint8_t* vp = vbn + join64(vlo[i], vhi[i]);
+      for (int h = 0; h < KCH; ++h) td.kd[KCH * i + h] = ld16(kp + 256 * h);
 #pragma unroll
-        for (int h = 0; h < VCH; ++h) td.vd[VCH * i + h] = ld16(vp + 256 * h);
-      }
+      for (int h = 0; h < VCH; ++h) td.vd[VCH * i + h] = ld16(vp + 256 * h);
     }
   };
 
@@ -541,13 +544,7 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     }
   };
 
-  Data db;
-#pragma unroll
-  for (int h = 0; h < 4 * VCH; ++h) db.vd[h] = (u32x4_t){0, 0, 0, 0};
-  if (VKLDS) {
-#pragma unroll
-    for (int q = 0; q < KSTEPS; ++q) db.kd[q] = (u32x4_t){0, 0, 0, 0};
-  }
+  Data db;   // every load_data call writes all of it
 
   // Gathers and consumes queued tokens, 16 at a time (all when flushing).
   auto run_queue = [&](bool flush) {
