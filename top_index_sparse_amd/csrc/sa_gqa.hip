@@ -7,11 +7,17 @@ namespace sa {
 
 namespace {
 
+// Waves per SIMD: two everywhere (the register budget of the products),
+// except the two-tile union team, which fits three (168 VGPRs, 4 spilled);
+// the third wave hides more of its per-tile latency (C2 union G=2 1.76 ->
+// 1.45 ms), where the per-token shapes lose more to spills than they gain.
 template <int MODE, int C, int WSPLIT>
 hipError_t launch(const AttnParams& p, hipStream_t stream) {
+  constexpr int kWaves = MODE == kUnion && C == 2 ? 3 : 2;
   dim3 grid, block;
   if (!attn_grid<WSPLIT>(p, MODE, &grid, &block)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_kernel<256, 256, false, MODE, C, WSPLIT, false, 2>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((attn_kernel<256, 256, false, MODE, C, WSPLIT, false, kWaves>), grid, block, 0,
+                     stream, p);
   return hipGetLastError();
 }
 
