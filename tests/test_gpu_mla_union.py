@@ -216,3 +216,22 @@ def test_union_gqa(Hq, Hkv, G):
     assert st == (sa.SA_OK if G * Hq // Hkv <= 32 else sa.SA_OK_FALLBACK)
     ro, rl = _oracle(case)
     check_close(out, lse, ro, rl, f"union gqa {Hq}/{Hkv} G={G}")
+
+
+@pytest.mark.parametrize("name,G", [("C2", 2), ("C1", 5)])
+def test_union_gqa_two_tile_full_size(name, G):
+    # the two-tile union team (G x group in 17..32 columns): C2 (2 KV heads x
+    # group 12) at G=2, C1 (group 6) at G=5, full size, sampled rows
+    say(f"[union] {name} G={G} full size, sampled rows vs oracle union attention")
+    case = config(name)
+    dev = attn_to_dev(case)
+    out, lse, st = _union(case, dev, G)
+    assert st == sa.SA_OK
+    rows = sample_rows(case.num_rows, 16)
+    ui, ub, ul = oracle.union_build(case.idx[: (rows.max() // G + 1) * G], case.kv_len, G)
+    ro, rl = oracle.union_attention(case.q, case.k, case.v, ui, ub, ul, G,
+                                    num_kv_heads=case.num_kv_heads, scale=case.scale, rows=rows)
+    sel = torch.from_numpy(rows).cuda()
+    e, el = check_close(out[sel], lse[sel], ro, rl, f"{name} union G={G}")
+    assert torch.isfinite(out).all()
+    say(f"  {name} G={G}: max abs err O {e:.2e} LSE {el:.2e}")

@@ -10,9 +10,10 @@
 //
 // gfx950 design.
 //
-// Teams. A team of WSPLIT wavefronts serves up to four query rows of one KV
-// head (consecutive rows in the per-token modes, members of one union group
-// in union mode) as C tiles of 16 columns, a column being one (row, head).
+// Teams. A team of WSPLIT wavefronts serves query rows of one KV head (up to
+// four consecutive rows in the per-token modes, up to eight members of one
+// union group in union mode) as C tiles of 16 columns, a column being one
+// (row, head).
 // Each wavefront computes half of the S^T k-steps and half of the O^T
 // d-columns when WSPLIT = 2 (the partial scores are summed through LDS, one
 // barrier per slot tile, in the same order in both wavefronts so their
