@@ -90,8 +90,10 @@ typedef enum { SA_DTYPE_BF16 = 1, SA_DTYPE_FP8_E4M3 = 2 } sa_dtype;
  * All strides are multiples of 8 elements (4 for out); kv_row_stride and
  * v_row_stride are below 2^31 elements (a K or V row fits 4 GiB).
  * Built shapes: (head_dim_qk, head_dim_v, v_in_k) = (256, 256, 0) with a
- * group of 1..16 query heads per KV head (PR 37275: group 6 and 12 at head
- * dim 256), and (576, 512, 1) with a group of 1..16 (PR 32779: 8 heads).
+ * group of 1..32 query heads per KV head (PR 37275: group 6 and 12 at head
+ * dim 256), and (576, 512, 1) with a group of 1..32 (PR 32779: 8 heads; more
+ * than 16 heads only over one latent KV head). 32 is the pages' cap on query
+ * heads per rank (PR 32779, "Robustness"); more is SA_ERR_UNSUPPORTED.
  */
 typedef struct {
   int32_t num_q_heads;

@@ -73,7 +73,7 @@ def test_validate_ok_shapes():
     (dict(sm_scale=math.inf), -2),
     (dict(head_dim_qk=128, head_dim_v=128, q_row_stride=768, kv_row_stride=128,
           v_row_stride=128, out_row_stride=768), -4),
-    (dict(num_q_heads=17, q_row_stride=17 * 256, out_row_stride=17 * 256), -4),
+    (dict(num_q_heads=33, q_row_stride=33 * 256, out_row_stride=33 * 256), -4),
     (dict(q_row_stride=6 * 256 - 8), -2),
     (dict(q_row_stride=6 * 256 + 4), -2),
     (dict(kv_row_stride=250), -2),
@@ -86,6 +86,20 @@ def test_validate_ok_shapes():
 def test_validate_rejects(kw, code):
     assert sa.sa_validate_attn(_desc(**kw)) == code
     assert sa.sa_last_error() != ""
+
+
+def test_wide_head_groups():
+    # up to 32 query heads per KV head; MLA above 16 heads needs one latent head
+    assert sa.sa_validate_attn(_desc(num_q_heads=32, q_row_stride=32 * 256,
+                                     out_row_stride=32 * 256)) == sa.SA_OK
+    assert sa.sa_validate_attn(_mla(num_q_heads=32, q_row_stride=32 * 576,
+                                    out_row_stride=32 * 512)) == sa.SA_OK
+    assert sa.sa_validate_attn(_mla(num_q_heads=48, num_kv_heads=2, q_row_stride=48 * 576,
+                                    kv_row_stride=2 * 576, out_row_stride=48 * 512)) == -4
+    # a 32-head group only fits union tiles of one row
+    d = _desc(num_q_heads=32, q_row_stride=32 * 256, out_row_stride=32 * 256)
+    assert sa.sa_validate_attn(d, 1) == sa.SA_OK
+    assert sa.sa_validate_attn(d, 2) == sa.SA_OK_FALLBACK
 
 
 def test_union_fallback_and_g_range():

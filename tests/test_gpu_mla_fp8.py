@@ -26,7 +26,7 @@ def _small(seed, T, kv, first, Hq, topk):
                               topk=topk, v_in_k=True, kv_fp8=True)
 
 
-@pytest.mark.parametrize("Hq", [8, 16, 3, 1])
+@pytest.mark.parametrize("Hq", [8, 16, 3, 1, 32])
 def test_fp8_small_padding_and_invalid(Hq):
     say(f"[fp8] MLA records, {Hq} heads: -1 padding, out-of-range, duplicates")
     c = _small(70 + Hq, 37, 400, 0, Hq, 256)

@@ -41,7 +41,7 @@ def test_mla_per_token_small_with_padding():
     check_close(out, lse, ro, rl, "mla small")
 
 
-@pytest.mark.parametrize("Hq", [8, 16, 3])
+@pytest.mark.parametrize("Hq", [8, 16, 3, 24, 32, 17])
 def test_mla_head_counts(Hq):
     say(f"[mla] {Hq} heads")
     case = _mla_small(32, 9, 3000, 2500, 2048, Hq=Hq)
@@ -205,7 +205,7 @@ def test_union_fallback_when_tile_illegal():
 
 
 @pytest.mark.parametrize("Hq,Hkv,G", [(6, 1, 2), (12, 2, 2), (4, 1, 4), (2, 1, 8), (6, 1, 5), (12, 1, 4),
-                                     (8, 1, 4), (12, 1, 2)])
+                                     (8, 1, 4), (12, 1, 2), (32, 1, 1), (40, 2, 1), (20, 1, 2)])
 def test_union_gqa(Hq, Hkv, G):
     say(f"[union] GQA d=256 group {Hq // Hkv} x {Hkv} KV heads, G={G}")
     case = gen.make_attn_case("u", seed=35 + G, num_rows=23, kv_len=3000, first_pos=2977,
@@ -235,3 +235,16 @@ def test_union_gqa_two_tile_full_size(name, G):
     e, el = check_close(out[sel], lse[sel], ro, rl, f"{name} union G={G}")
     assert torch.isfinite(out).all()
     say(f"  {name} G={G}: max abs err O {e:.2e} LSE {el:.2e}")
+
+
+@pytest.mark.parametrize("Hq,G", [(24, 1), (32, 1), (32, 2)])
+def test_mla_wide_head_rows_union(Hq, G):
+    # more than 16 heads: two 16-head slices; G=2 is illegal (64 rows) and
+    # falls back to the per-token path
+    say(f"[union] MLA {Hq} heads, G={G}")
+    case = _mla_small(36, 11, 2000, 1900, 300, Hq=Hq)
+    dev = attn_to_dev(case)
+    out, lse, st = _union(case, dev, G)
+    assert st == (sa.SA_OK if G * Hq <= 32 else sa.SA_OK_FALLBACK)
+    ro, rl = _oracle(case)
+    check_close(out, lse, ro, rl, f"mla {Hq} heads G={G}")

@@ -47,7 +47,8 @@ def _small(seed, T, kv, first, Hq, Hkv, topk, walk=True):
                               head_dim_v=256, topk=topk, walk=walk)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(6, 1), (12, 1), (24, 2), (1, 1), (16, 1), (9, 3), (4, 2)])
+@pytest.mark.parametrize("Hq,Hkv", [(6, 1), (12, 1), (24, 2), (1, 1), (16, 1), (9, 3), (4, 2),
+                                    (20, 1), (32, 1), (50, 2), (64, 2)])
 def test_groups_and_ragged_tail_tile(Hq, Hkv):
     # 2051 = 128 * 16 + 3 slots: a 3-slot tail tile; 37 rows: 4-row groups with a tail
     say(f"[prefill] group {Hq // Hkv} x {Hkv} KV heads, topk 2051")
@@ -207,6 +208,18 @@ def test_chunk_prefill_small_ragged():
     ro, rl = oracle.chunk_prefill(case.q, case.k, case.v, case.idx, case.cu_seqlens_q,
                                   case.cu_seqlens_kv, num_kv_heads=1, scale=case.scale)
     check_close(out, lse, ro, rl, "ragged small")
+
+
+def test_chunk_prefill_ragged_group_32():
+    say("[chunk] ragged batch, 32 query heads over one KV head (one row per team)")
+    case = gen.make_ragged_case("r32", seed=23, num_reqs=4, qlen_range=(3, 30),
+                                ctx_range=(200, 700), num_q_heads=32, num_kv_heads=1,
+                                head_dim=256, topk=150)
+    dev = attn_to_dev(case)
+    out, lse = _chunk(case, dev)
+    ro, rl = oracle.chunk_prefill(case.q, case.k, case.v, case.idx, case.cu_seqlens_q,
+                                  case.cu_seqlens_kv, num_kv_heads=1, scale=case.scale)
+    check_close(out, lse, ro, rl, "ragged group 32")
 
 
 def test_chunk_prefill_c4_sampled():

@@ -30,11 +30,11 @@ def _case(i):
     mla = bool(rng.integers(0, 3) == 0)
     fp8 = mla and bool(rng.integers(0, 2))
     if mla:
-        hkv, hq = 1, int(rng.choice([1, 2, 3, 5, 8, 13, 16]))
+        hkv, hq = 1, int(rng.choice([1, 2, 3, 5, 8, 13, 16, 24, 32]))
         dqk, dv = 576, 512
     else:
         hkv = int(rng.choice([1, 2, 3]))
-        hq = hkv * int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 16]))
+        hq = hkv * int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 16, 20, 27, 32]))
         dqk = dv = 256
     kv = int(rng.integers(1, 700))
     T = int(rng.integers(1, 70))

@@ -62,7 +62,11 @@ sa_status check_desc(const sa_attn_desc* d, int32_t G, Kernel* kernel) {
   }
   if (fp8 && *kernel != Kernel::kMla576Fp8)
     return fail(SA_ERR_DTYPE, "FP8 K is accepted as 656-byte MLA records (576/512, v_in_k) only");
-  if (group > 16) return fail(SA_ERR_UNSUPPORTED, "group %d > 16 query heads per KV head", group);
+  // at most 32 query heads per KV head, the pages' cap; an MLA row of more
+  // than 16 heads runs as two 16-head slices over its one latent head
+  if (group > 32) return fail(SA_ERR_UNSUPPORTED, "group %d > 32 query heads per KV head", group);
+  if (d->v_in_k && group > 16 && d->num_kv_heads != 1)
+    return fail(SA_ERR_UNSUPPORTED, "MLA with %d > 16 query heads needs one latent KV head", group);
   const int64_t qrow = (int64_t)d->num_q_heads * d->head_dim_qk;
   const int64_t krow = (int64_t)d->num_kv_heads * d->head_dim_qk;
   const int64_t vrow = (int64_t)d->num_kv_heads * d->head_dim_v;
@@ -123,6 +127,7 @@ sa::AttnParams make_params(const sa_attn_desc* d, const void* q, const void* k, 
   p.v_row_stride = d->v_in_k ? kstride : d->v_row_stride;
   p.idx_row_stride = d->idx_row_stride;
   p.out_row_stride = d->out_row_stride;
+  p.lse_row_stride = d->num_q_heads;
   p.num_rows = num_rows;
   p.topk = d->topk;
   p.num_q_heads = d->num_q_heads;
@@ -490,6 +495,8 @@ sa_status sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_page_desc*
   if (desc->num_kv_heads != 1)
     return fail(SA_ERR_SHAPE, "a page row holds one latent record per token: num_kv_heads %d != 1",
                 desc->num_kv_heads);
+  if (desc->num_q_heads > 16)
+    return fail(SA_ERR_UNSUPPORTED, "decode takes at most 16 query heads (%d)", desc->num_q_heads);
   if (!pages) return fail(SA_ERR_NULL, "pages is NULL");
   const int32_t ptok = pages->dst_page_tokens;
   if (ptok <= 0 || (ptok & (ptok - 1)) || ptok > (1 << 20))

@@ -633,7 +633,7 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
         }
       }
       if (g == 0 && split == 0)
-        p.lse[(int64_t)t * p.num_q_heads + head] =
+        p.lse[(int64_t)t * p.lse_row_stride + head] =
             l > 0.f ? (m_run[c] + fast_log2(l)) * kLn2 : -INFINITY;
     }
   }

@@ -22,6 +22,7 @@ struct AttnParams {
   int64_t v_row_stride;
   int64_t idx_row_stride;
   int64_t out_row_stride;
+  int64_t lse_row_stride;     // lse[t * lse_row_stride + head]
   int32_t num_rows;
   int32_t num_reqs;
   int32_t kv_len;             // non-ragged KV length
