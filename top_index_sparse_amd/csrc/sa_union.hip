@@ -305,16 +305,32 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuild
   const int nchunks = kv_len > 0 ? (kv_len + cap - 1) / cap : 0;
 
   // Clears the planes, then marks every member's indices in [c0, c0 + 32 W).
+  // A batch reads KB indices of every member before it marks any, so about
+  // eight loads per thread are in flight instead of one.
+  constexpr int KB = M >= 8 ? 1 : 8 / M;
   auto mark = [&](int c0, int W) {
     for (int i = tid; i < members * W; i += kBitmapThreads) planes[i] = 0u;
     __syncthreads();
-    for (int j = 0; j < members; ++j) {
-      const int32_t* row = p.idx + (int64_t)(first + j) * p.idx_row_stride;
-      uint32_t* plane = planes + j * W;
-      for (int e = tid; e < p.topk; e += kBitmapThreads) {
-        const int32_t x = row[e];
-        const uint32_t o = (uint32_t)(x - c0);
-        if ((unsigned)x < (unsigned)kv_len && o < (uint32_t)(32 * W)) atomicOr(&plane[o >> 5], 1u << (o & 31));
+    for (int e0 = 0; e0 < p.topk; e0 += KB * kBitmapThreads) {
+      int32_t x[M][KB];
+#pragma unroll
+      for (int j = 0; j < M; ++j) {
+        const int32_t* row = p.idx + (int64_t)(first + (j < members ? j : 0)) * p.idx_row_stride;
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+          const int e = e0 + tid + u * kBitmapThreads;
+          x[j][u] = j < members && e < p.topk ? row[e] : -1;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < M; ++j) {
+        uint32_t* plane = planes + j * W;
+#pragma unroll
+        for (int u = 0; u < KB; ++u) {
+          const uint32_t o = (uint32_t)(x[j][u] - c0);
+          if ((unsigned)x[j][u] < (unsigned)kv_len && o < (uint32_t)(32 * W))
+            atomicOr(&plane[o >> 5], 1u << (o & 31));
+        }
       }
     }
     __syncthreads();
