@@ -1,5 +1,6 @@
-// Device helpers shared by the gfx950 kernels: vector types, 16-byte loads,
-// bf16 packing, MFMA wrappers, XCD-aware block remapping.
+// Device helpers shared by the gfx950 kernels: vector types, DPP wave
+// scans, 16-byte loads, bf16 packing, MFMA wrappers, XCD-aware block
+// remapping.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,6 +17,28 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
+
+// Inclusive prefix sums within each row of 16 lanes (DPP row shifts; lanes
+// shifted in from outside the row add 0).
+__device__ __forceinline__ uint32_t row_scan16(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  return x;
+}
+
+// Inclusive prefix sums over the wave's 64 lanes: the rows' own scans, then
+// row_bcast:15 adds row 0's total to row 1 and row 2's to row 3, and
+// row_bcast:31 adds the total of rows 0-1 to rows 2 and 3 (the other rows
+// are masked off and add 0).
+__device__ __forceinline__ uint32_t wave_scan64(uint32_t x) {
+  x = row_scan16(x);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);
+  return x;
+}
+
 
 __device__ __forceinline__ u32x4_t ld16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);

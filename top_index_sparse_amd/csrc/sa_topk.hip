@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sa_device.h"
 #include "sa_internal.h"
 
 namespace sa {
@@ -59,27 +60,6 @@ struct TopkLds {
   uint32_t wsel[kBatch * kWaves + 1];   // output: (chunk, wave) totals, then bases
   uint32_t wtie[kBatch * kWaves + 1];
 };
-
-// Inclusive prefix sums within each row of 16 lanes (DPP row shifts; lanes
-// shifted in from outside the row add 0).
-__device__ __forceinline__ uint32_t row_scan16(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
-  return x;
-}
-
-// Inclusive prefix sums over the wave's 64 lanes: the rows' own scans, then
-// row_bcast:15 adds row 0's total to row 1 and row 2's to row 3, and
-// row_bcast:31 adds the total of rows 0-1 to rows 2 and 3 (the other rows
-// are masked off and add 0).
-__device__ __forceinline__ uint32_t wave_scan64(uint32_t x) {
-  x = row_scan16(x);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);
-  return x;
-}
 
 // OR of lanes 8j .. 8j+7 in lane 8j+7 (groups of 8 lie inside a DPP row).
 __device__ __forceinline__ uint32_t or8_into_top(uint32_t v) {

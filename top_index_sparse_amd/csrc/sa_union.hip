@@ -335,12 +335,22 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuild
     }
     __syncthreads();
   };
-  // Each thread owns a contiguous range of words; counts its tokens per
-  // bucket (the bucket of a token is its lowest owning member).
-  auto count = [&](int W, int w0, int w1, int cnt[M]) {
+  // Wave v owns the contiguous words [wb, we) of a chunk and reads them 64 at
+  // a time, lane l taking word wb + 64 r + l in round r: a round's tokens of
+  // one bucket then go to consecutive list positions (the bucket of a token
+  // is its lowest owning member). count: this lane's tokens per bucket.
+  const int lane = tid & 63, wave = tid >> 6;
+  auto wave_words = [&](int W, int& wb, int& we) {
+    const int per = (W + kBitmapThreads / 64 - 1) / (kBitmapThreads / 64);
+    wb = min(W, wave * per);
+    we = min(W, wb + per);
+  };
+  auto count = [&](int W, int cnt[M]) {
 #pragma unroll
     for (int j = 0; j < M; ++j) cnt[j] = 0;
-    for (int w = w0; w < w1; ++w) {
+    int wb, we;
+    wave_words(W, wb, we);
+    for (int w = wb + lane; w < we; w += 64) {
       uint32_t seen = 0u;
 #pragma unroll
       for (int j = 0; j < M; ++j) {
@@ -353,11 +363,6 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuild
     }
   };
   auto words = [&](int c) { const int left = (kv_len - c * cap + 31) >> 5; return left < p.plane_words ? left : p.plane_words; };
-  auto range = [&](int W, int& w0, int& w1) {
-    const int wpt = (W + kBitmapThreads - 1) / kBitmapThreads;
-    w0 = min(W, tid * wpt);
-    w1 = min(W, w0 + wpt);
-  };
 
   int total[M];
 #pragma unroll
@@ -365,10 +370,9 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuild
   if (nchunks > 1) {
     for (int c = 0; c < nchunks; ++c) {
       const int W = words(c);
-      int w0, w1, cnt[M], excl[M], tot[M];
-      range(W, w0, w1);
+      int cnt[M], excl[M], tot[M];
       mark(c * cap, W);
-      count(W, w0, w1, cnt);
+      count(W, cnt);
       scan_buckets<M>(cnt, excl, tot, wave_tot);
 #pragma unroll
       for (int j = 0; j < M; ++j) total[j] += tot[j];
@@ -381,10 +385,9 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuild
   for (int c = 0; c < nchunks; ++c) {
     const int W = words(c);
     const int c0 = c * cap;
-    int w0, w1, cnt[M], excl[M], tot[M];
-    range(W, w0, w1);
+    int cnt[M], excl[M], tot[M];
     mark(c0, W);
-    count(W, w0, w1, cnt);
+    count(W, cnt);
     scan_buckets<M>(cnt, excl, tot, wave_tot);
     if (nchunks == 1) {
 #pragma unroll
@@ -398,27 +401,36 @@ __global__ void __launch_bounds__(kBitmapThreads) union_bitmap_kernel(UnionBuild
       acc += total[j];
     }
     len = acc;
-    int pos[M];
+    // this wave's first position per bucket (lane 0's exclusive prefix: the
+    // tokens of the earlier waves), advanced round by round
+    int at0[M];
 #pragma unroll
-    for (int j = 0; j < M; ++j) pos[j] = base[j] + carry[j] + excl[j];
-    for (int w = w0; w < w1; ++w) {
+    for (int j = 0; j < M; ++j) at0[j] = base[j] + carry[j] + __builtin_amdgcn_readlane(excl[j], 0);
+    int wb, we;
+    wave_words(W, wb, we);
+    for (int r0 = wb; r0 < we; r0 += 64) {
+      const int w = r0 + lane;
       uint32_t b[M];
 #pragma unroll
-      for (int j = 0; j < M; ++j) b[j] = j < members ? planes[j * W + w] : 0u;
+      for (int j = 0; j < M; ++j) b[j] = j < members && w < we ? planes[j * W + w] : 0u;
       uint32_t seen = 0u;
 #pragma unroll
       for (int j = 0; j < M; ++j) {
         uint32_t fresh = b[j] & ~seen;
         seen |= b[j];
+        const uint32_t n = (uint32_t)__popc(fresh);
+        const uint32_t incl = wave_scan64(n);
+        int at = at0[j] + (int)(incl - n);
+        at0[j] += __builtin_amdgcn_readlane((int)incl, 63);
         while (fresh) {
           const int bit = __builtin_ctz(fresh);
           fresh &= fresh - 1u;
           uint32_t own = 0u;
 #pragma unroll
           for (int jj = 0; jj < M; ++jj) own |= ((b[jj] >> bit) & 1u) << jj;
-          uidx[pos[j]] = c0 + w * 32 + bit;
-          ubits[pos[j]] = (uint8_t)own;
-          ++pos[j];
+          uidx[at] = c0 + w * 32 + bit;
+          ubits[at] = (uint8_t)own;
+          ++at;
         }
       }
     }
