@@ -302,3 +302,25 @@ def test_team_rows_position_sharing(Hq):
                                           sm_scale=case.scale)
     torch.cuda.synchronize()
     check_close(o2, l2, ro, rl, f"team rows ragged group {Hq}")
+
+
+def test_binding_rejects_undersized_outputs():
+    say("[binding] caller outputs too small: ValueError before any launch")
+    case = _small(41, 8, 500, 400, 6, 1, 64)
+    dev = attn_to_dev(case)
+    before = sa.sa_call_count("sparse_attn_prefill")
+    with pytest.raises(ValueError):
+        sa.sparse_attn_prefill(dev["q"], dev["k"], dev["v"], dev["idx"],
+                               out=torch.empty((7, 6, 256), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        sa.sparse_attn_prefill(dev["q"], dev["k"], dev["v"], dev["idx"],
+                               lse=torch.empty((8, 5), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        sa.sparse_attn_union_build(dev["idx"], 500, 2,
+                                   union_len=torch.empty((3,), dtype=torch.int32, device="cuda"))
+    with pytest.raises(ValueError):
+        sa.indexer_topk(torch.zeros((4, 100), dtype=torch.float32, device="cuda"), 10,
+                        out=torch.empty((4, 9), dtype=torch.int32, device="cuda"))
+    with pytest.raises(ValueError):
+        sa.sparse_attn_prefill_union(dev["q"], dev["k"], dev["v"], dev["idx"], 2, kv_len=501)
+    assert sa.sa_call_count("sparse_attn_prefill") == before

@@ -181,6 +181,14 @@ def _need(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _need_size(t: torch.Tensor, name: str, rows: int, inner: Tuple[int, ...]):
+    """At least `rows` rows, and exactly the given inner dims: the kernels
+    write rows 0 .. rows - 1 at the tensor's row stride."""
+    if t.shape[0] < rows or tuple(t.shape[1:]) != tuple(inner):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, needs [>= {rows}, "
+                         f"{', '.join(str(d) for d in inner)}]")
+
+
 def _rows_dense(t: torch.Tensor, name: str):
     """Inner dims contiguous; the row stride is free."""
     if t.dim() >= 2 and t.numel() > 0:
@@ -239,6 +247,8 @@ def _prep_attn(q, k, v, idx, sm_scale, head_dim_v, out, lse, num_rows):
         lse = torch.empty((num_rows, q.shape[1]), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.float32, 3, q.device)
     _need(lse, "lse", torch.float32, 2, q.device)
+    _need_size(out, "out", num_rows, (q.shape[1], head_dim_v))
+    _need_size(lse, "lse", num_rows, (q.shape[1],))
     _rows_dense(out, "out")
     if not lse.is_contiguous():
         raise ValueError("lse must be contiguous")
@@ -333,9 +343,16 @@ def sparse_attn_union_build(idx: torch.Tensor, kv_len: int, G: int, *,
         union_bits = torch.empty((ng, G * K), dtype=torch.uint8, device=dev)
     if union_len is None:
         union_len = torch.empty((ng,), dtype=torch.int32, device=dev)
-    for t, name in ((union_idx, "union_idx"), (union_bits, "union_bits"), (union_len, "union_len")):
-        if not t.is_contiguous() or t.device != dev:
-            raise ValueError(f"{name} must be contiguous on {dev}")
+    for t, name, dtype in ((union_idx, "union_idx", torch.int32), (union_bits, "union_bits", torch.uint8),
+                           (union_len, "union_len", torch.int32)):
+        if not t.is_contiguous() or t.device != dev or t.dtype != dtype:
+            raise ValueError(f"{name} must be a contiguous {dtype} tensor on {dev}")
+    if union_idx.dim() != 2 or union_bits.dim() != 2:
+        raise ValueError("union_idx and union_bits are [groups, G * topk] tensors")
+    _need_size(union_idx, "union_idx", ng, (G * K,))
+    _need_size(union_bits, "union_bits", ng, (G * K,))
+    if union_len.numel() < ng:
+        raise ValueError(f"union_len holds {union_len.numel()} entries, needs {ng}")
     nbytes = sparse_attn_union_workspace_bytes(T, K, G)
     ws = _workspace(ws, nbytes, dev)
     st = lib().sparse_attn_union_build(_ptr(idx), idx.stride(0), T, K, int(kv_len), G,
@@ -356,6 +373,8 @@ def sparse_attn_prefill_union(q: torch.Tensor, k: torch.Tensor, v: Optional[torc
     T = q.shape[0]
     desc, out, lse = _prep_attn(q, k, v, idx, sm_scale, head_dim_v, out, lse, T)
     kv_len = k.shape[0] if kv_len is None else int(kv_len)
+    if kv_len > k.shape[0]:
+        raise ValueError(f"kv_len {kv_len} > k rows {k.shape[0]}")
     nbytes = sparse_attn_union_workspace_bytes(T, idx.shape[1], G)
     ws = _workspace(ws, nbytes, q.device)
     st = lib().sparse_attn_prefill_union(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
@@ -480,6 +499,8 @@ def sparse_attn_decode_paged(q: torch.Tensor, pool: torch.Tensor, idx: torch.Ten
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.float32, 3, q.device)
     _need(lse, "lse", torch.float32, 2, q.device)
+    _need_size(out, "out", B, (Hq, 512))
+    _need_size(lse, "lse", B, (Hq,))
     _rows_dense(out, "out")
     if not lse.is_contiguous():
         raise ValueError("lse must be contiguous")
@@ -516,6 +537,8 @@ def indexer_topk(scores: torch.Tensor, k: int, *, row_len: Optional[torch.Tensor
     if out is None:
         out = torch.empty((T, k), dtype=torch.int32, device=scores.device)
     _need(out, "out", torch.int32, 2, scores.device)
+    if out.shape[0] < T or out.shape[1] < k:
+        raise ValueError(f"out has shape {tuple(out.shape)}, needs at least [{T}, {k}]")
     _rows_dense(out, "out")
     st = lib().indexer_topk(_ptr(scores), scores.stride(0) if T > 0 else kv, _ptr(row_len), T, kv,
                             int(k), _ptr(out), out.stride(0) if T > 0 else k, _stream(stream))
