@@ -453,6 +453,11 @@ def page_split(src: torch.Tensor, dst: torch.Tensor, mask: Optional[torch.Tensor
     P = src.shape[0]
     if dst.shape[0] < P * (src_page_tokens // max(dst_page_tokens, 1)):
         raise ValueError("dst has fewer pages than the split produces")
+    if mask is not None and mask.shape[0] < P:
+        raise ValueError(f"mask holds {mask.shape[0]} pages, src has {P}")
+    if src.shape[1] < src_page_tokens * (row_bytes + scale_bytes) or \
+            dst.shape[1] < dst_page_tokens * (row_bytes + scale_bytes):
+        raise ValueError("a src or dst row is narrower than one page")
     st = lib().page_split(ctypes.byref(desc), _ptr(src), _ptr(dst), _ptr(mask), P,
                           _stream(stream))
     _check(st, "page_split")
@@ -487,6 +492,8 @@ def sparse_attn_decode_paged(q: torch.Tensor, pool: torch.Tensor, idx: torch.Ten
     B, Hq = q.shape[0], q.shape[1]
     if idx.shape[0] != B:
         raise ValueError(f"idx rows {idx.shape[0]} != batch {B}")
+    if pool.shape[1] < dst_page_tokens * (FP8_RECORD_BYTES + scale_bytes):
+        raise ValueError(f"pool rows of {pool.shape[1]} B are narrower than one page")
     if topk_len is not None:
         _need(topk_len, "topk_len", torch.int32, 1, q.device)
         if topk_len.shape[0] != B or not topk_len.is_contiguous():
