@@ -172,6 +172,8 @@ size_t sparse_attn_union_workspace_bytes(int32_t num_rows, int32_t topk, int32_t
  * ws          device workspace of sparse_attn_union_workspace_bytes bytes,
  *             used only during the call
  * G           1..8
+ * topk        1..8192 (the sort path holds a row's padded keys in 32 KB of
+ *             LDS); a larger topk returns SA_ERR_SHAPE
  * Output is bit-exact and deterministic.
  */
 sa_status sparse_attn_union_build(const int32_t* idx, int64_t idx_row_stride, int32_t num_rows,
@@ -185,7 +187,8 @@ sa_status sparse_attn_union_build(const int32_t* idx, int64_t idx_row_stride, in
  * to -inf where its ownership bit is clear, so every row's result is that of
  * the per-token path over its distinct valid indices.
  * Legal iff G * group <= 32; otherwise the per-token path runs instead and
- * SA_OK_FALLBACK is returned (PR 32779, review item 1).
+ * SA_OK_FALLBACK is returned (PR 32779, review item 1). topk is at most 8192,
+ * as for sparse_attn_union_build (SA_ERR_SHAPE above).
  * ws  device workspace of sparse_attn_union_workspace_bytes(num_rows, topk, G)
  */
 sa_status sparse_attn_prefill_union(const sa_attn_desc* desc, const void* q, const void* k,
