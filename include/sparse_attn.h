@@ -282,7 +282,7 @@ size_t sparse_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, in
  * not read: each record carries the scales of all its FP8 values.
  *
  * desc   head dims (576, 512), v_in_k = 1, num_kv_heads = 1, num_q_heads
- *        1..16, kv_dtype SA_DTYPE_FP8_E4M3, kv_row_stride = 656; topk,
+ *        1..32, kv_dtype SA_DTYPE_FP8_E4M3, kv_row_stride = 656; topk,
  *        sm_scale and the q, idx, out row strides as for prefill
  * pages  dst_page_tokens (a power of two), row_bytes = 656, scale_bytes,
  *        dst_page_stride (>= dst_page_tokens * (row_bytes + scale_bytes), a

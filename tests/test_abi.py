@@ -264,7 +264,9 @@ def test_decode_workspace_bytes():
     # batch 512 x 2048 slots: 128 tiles need 16 ranges of 8
     assert sa.sparse_attn_decode_workspace_bytes(512, 1, 2048) == 512 * 16 * 2048 + 32768
     assert sa.sparse_attn_decode_workspace_bytes(0, 8, 2048) == 0
-    assert sa.sparse_attn_decode_workspace_bytes(4, 17, 2048) == 0
+    # 32 heads (two 16-head slices of one launch each): batch 4 -> 128 ranges
+    assert sa.sparse_attn_decode_workspace_bytes(4, 32, 2048) == 4 * 128 * 32 * 2048 + 4 * 128 * 32 * 4
+    assert sa.sparse_attn_decode_workspace_bytes(4, 33, 2048) == 0
     assert sa.sparse_attn_decode_workspace_bytes(4, 8, 0) == 0
 
 

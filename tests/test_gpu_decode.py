@@ -33,7 +33,8 @@ def _indices(rng, B, topk, tokens):
 
 
 @pytest.mark.parametrize("B,Hq,topk,ptok", [(1, 8, 2048, 64), (3, 16, 100, 64), (37, 3, 256, 64),
-                                            (5, 1, 16, 16), (64, 8, 300, 128), (300, 8, 33, 64)])
+                                            (5, 1, 16, 16), (64, 8, 300, 128), (300, 8, 33, 64),
+                                            (4, 32, 512, 64), (7, 17, 200, 64), (2, 24, 2048, 64)])
 def test_decode_pool(B, Hq, topk, ptok):
     say(f"[decode] batch {B}, {Hq} heads, topk {topk}, {ptok}-token pages, padded stride")
     rng = np.random.default_rng(B * 1000 + Hq * 10 + topk)

@@ -228,7 +228,7 @@ struct DecodeLayout {
 };
 
 bool decode_layout(int32_t batch, int32_t num_q_heads, int32_t topk, DecodeLayout* L) {
-  if (batch < 0 || num_q_heads <= 0 || num_q_heads > 16 || topk <= 0) return false;
+  if (batch < 0 || num_q_heads <= 0 || num_q_heads > 32 || topk <= 0) return false;
   const int64_t tiles = ((int64_t)topk + 15) / 16;
   int64_t s = batch > 0 ? (kDecodeTeams + batch - 1) / batch : 1;
   const int64_t s_min = (tiles + kDecodeTilesPerRange - 1) / kDecodeTilesPerRange;
@@ -495,8 +495,6 @@ sa_status sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_page_desc*
   if (desc->num_kv_heads != 1)
     return fail(SA_ERR_SHAPE, "a page row holds one latent record per token: num_kv_heads %d != 1",
                 desc->num_kv_heads);
-  if (desc->num_q_heads > 16)
-    return fail(SA_ERR_UNSUPPORTED, "decode takes at most 16 query heads (%d)", desc->num_q_heads);
   if (!pages) return fail(SA_ERR_NULL, "pages is NULL");
   const int32_t ptok = pages->dst_page_tokens;
   if (ptok <= 0 || (ptok & (ptok - 1)) || ptok > (1 << 20))

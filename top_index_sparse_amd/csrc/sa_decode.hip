@@ -115,13 +115,21 @@ __global__ void __launch_bounds__(kCombineThreads) decode_combine_kernel(DecodeC
 hipError_t launch_decode_mla576_fp8(AttnParams p, const DecodeCombineParams& c,
                                     hipStream_t stream) {
   p.rows_per_team = 1;
-  dim3 grid, block;
-  if (!attn_grid<2>(p, kRows, &grid, &block)) return hipErrorInvalidConfiguration;
-  // one team per (request, range)
-  hipLaunchKernelGGL((attn_kernel<576, 512, true, kDecode, 1, 2, true, 2>), grid, block, 0, stream,
-                     p);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // one team per (request, range); more than 16 heads run as 16-head
+  // slices, each writing its heads' columns of the partial results
+  for (int h0 = 0; h0 < p.group; h0 += 16) {
+    AttnParams ps = p;
+    ps.group = ps.num_q_heads = p.group - h0 < 16 ? p.group - h0 : 16;
+    ps.q = p.q + (int64_t)h0 * 576;
+    ps.out = p.out + (int64_t)h0 * 512;
+    ps.lse = p.lse + h0;
+    dim3 grid, block;
+    if (!attn_grid<2>(ps, kRows, &grid, &block)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((attn_kernel<576, 512, true, kDecode, 1, 2, true, 2>), grid, block, 0,
+                       stream, ps);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t blocks = (int64_t)c.batch * c.num_q_heads;
   if (blocks * kCombineThreads > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)blocks),
