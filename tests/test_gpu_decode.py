@@ -96,3 +96,33 @@ def test_decode_after_mark_and_split(name):
                                  scale=c.scale)
     e, el = check_close(out, lse, ro, rl, f"{name} decode")
     say(f"  {name}: {int(m.sum())} touched pages; max abs err O {e:.2e} LSE {el:.2e}")
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_decode_sweep(i):
+    """Seeded random decode cases: batch, 1-32 heads, top-k, page size, pool
+    stride, top-k lengths, -1, out-of-range and duplicated slots."""
+    rng = np.random.default_rng(5000 + i)
+    B = int(rng.integers(1, 70))
+    Hq = int(rng.integers(1, 33))
+    topk = int(rng.integers(1, 1200))
+    ptok = int(rng.choice([16, 32, 64, 128]))
+    pages = int(rng.integers(1, 5000 // ptok + 2))
+    stride = ptok * 660 + 16 * int(rng.integers(0, 9))
+    say(f"[decode sweep {i}] B={B} Hq={Hq} topk={topk} ptok={ptok} pages={pages} stride={stride}")
+    pool = _pool(rng, pages, ptok, stride)
+    q = gen.normal_bf16(rng, (B, Hq, 576))
+    idx = rng.integers(0, pages * ptok, size=(B, topk)).astype(np.int32)
+    m = rng.random(idx.shape)
+    idx[m < 0.2] = -1
+    idx[(m >= 0.2) & (m < 0.23)] = pages * ptok + int(rng.integers(0, 99))
+    if topk > 2:
+        idx[:, 1] = idx[:, 0]
+    tl = rng.integers(-3, topk + 5, B).astype(np.int32) if rng.random() < 0.5 else None
+    scale = float(rng.uniform(0.02, 0.08))
+    out, lse = sa.sparse_attn_decode_paged(bf16_dev(q), _u8(pool), i32_dev(idx),
+                                           dst_page_tokens=ptok, sm_scale=scale,
+                                           topk_len=None if tl is None else i32_dev(tl))
+    torch.cuda.synchronize()
+    ro, rl = oracle.paged_decode(q, pool, idx, page_tokens=ptok, scale=scale, topk_len=tl)
+    check_close(out, lse, ro, rl, f"decode sweep {i}")
