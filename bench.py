@@ -1,6 +1,6 @@
 """Benchmark: sparse GQA chunk prefill, 8192 rows x 2051 slots, on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 10]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 100]
 
 One step is one sparse_attn_chunk_prefill call over the 8192-row workload
 (one request at the end of a 32768-token context, top-k 2051 random-walk
