@@ -15,7 +15,7 @@ from tests.gpu_util import bf16_dev, check_close, i32_dev, i64_dev, say
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 60
+N_CASES = 100
 
 
 def _padded(t, extra):

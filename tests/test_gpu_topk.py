@@ -84,3 +84,28 @@ def test_topk_counts_past_16_bits():
     s[1] = -2.5
     _check(s, k, np.array([kv, kv, 69999], np.int32), "k=66000")
     _check(s[:2], 2051, None, "70000 ties")
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_topk_sweep(i):
+    """Seeded random shapes and score kinds: N(0,1), heavy ties, one value,
+    fp32 subnormals, and a mix of +-inf, +-0 and +-1."""
+    rng = np.random.default_rng(90000 + i)
+    T = int(rng.integers(1, 9))
+    kv = int(rng.choice([rng.integers(1, 600), rng.integers(600, 40000), rng.integers(40000, 90000)]))
+    k = int(rng.integers(1, min(kv + 100, 9000)))
+    kind = int(rng.integers(0, 5))
+    if kind == 0:
+        s = rng.standard_normal((T, kv))
+    elif kind == 1:
+        s = np.round(rng.standard_normal((T, kv)) * 2) / 2
+    elif kind == 2:
+        s = np.full((T, kv), float(rng.standard_normal()))
+    elif kind == 3:
+        s = rng.standard_normal((T, kv)) * 1e-40
+    else:
+        s = rng.choice([-np.inf, np.inf, 0.0, -0.0, 1.0, -1.0], size=(T, kv))
+    s = s.astype(np.float32)
+    rl = rng.integers(-5, kv + 20, T).astype(np.int32) if rng.random() < 0.6 else None
+    say(f"[topk sweep {i}] T={T} kv={kv} k={k} kind={kind} row_len={rl is not None}")
+    _check(s, k, rl, f"sweep {i}")
