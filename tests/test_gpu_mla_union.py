@@ -94,6 +94,31 @@ def test_union_build_random_exact(T, k, kv, G):
     _check_union_exact(idx, kv, G)
 
 
+@pytest.mark.parametrize("i", range(40))
+def test_union_build_sweep(i):
+    """Seeded random T, top-k, kv_len (both build paths, up to 3M tokens) and
+    G in 1..8; half the cases give neighbouring rows mostly the same slots."""
+    rng = np.random.default_rng(70000 + i)
+    T = int(rng.integers(1, 80))
+    k = int(rng.integers(1, 2600))
+    kv = int(rng.choice([rng.integers(1, 3000), rng.integers(3000, 300000),
+                         rng.integers(300000, 3000000)]))
+    G = int(rng.integers(1, 9))
+    idx = rng.integers(-3, kv + 4, size=(T, k)).astype(np.int32)
+    if rng.random() < 0.5:
+        base = np.sort(rng.choice(kv, size=min(k, kv), replace=False)) if kv >= k \
+            else rng.integers(0, kv, k)
+        for t in range(T):
+            row = np.array(base[:k], dtype=np.int64)
+            m = rng.random(len(row)) < 0.05
+            row[m] = rng.integers(-1, kv, m.sum())
+            idx[t, :len(row)] = row
+    if k > 4:
+        idx[0, :2] = idx[0, 2]
+    say(f"[union build sweep {i}] T={T} k={k} kv={kv} G={G}")
+    _check_union_exact(idx, kv, G)
+
+
 @pytest.mark.parametrize("G", [2, 4])
 def test_union_build_c3_exact(G):
     say(f"[union build] C3 full size G={G}, bit-exact")
