@@ -253,14 +253,16 @@ def test_fp8_records_validation():
 
 
 def test_decode_workspace_bytes():
-    # ~1024 (request, range) teams, each range at most 8 of a request's 16-slot
-    # tiles: batch 32 x 2048 slots -> 32 ranges; partial O [1024][8][512]
+    # ~512 (request, range) teams, each range at most 8 of a request's 16-slot
+    # tiles: batch 32 x 2048 slots -> 16 ranges; partial O [512][8][512]
     # fp32, then LSE
-    assert sa.sparse_attn_decode_workspace_bytes(32, 8, 2048) == 32 * 32 * 8 * 2048 + 32 * 32 * 8 * 4
+    assert sa.sparse_attn_decode_workspace_bytes(32, 8, 2048) == 32 * 16 * 8 * 2048 + 32 * 16 * 8 * 4
     # batch 1: one range per tile (128 ranges)
     assert sa.sparse_attn_decode_workspace_bytes(1, 8, 2048) == 128 * 8 * 2048 + 4096
-    # batch 512: at least 2 ranges per request; 7 tiles of slots -> 2 ranges
-    assert sa.sparse_attn_decode_workspace_bytes(512, 2, 100) == 1024 * 2 * 2048 + 8192
+    # batch 512: one range per request; 7 tiles of slots -> 1 range
+    assert sa.sparse_attn_decode_workspace_bytes(512, 2, 100) == 512 * 2 * 2048 + 4096
+    # batch 8: 64 ranges of 2 tiles each
+    assert sa.sparse_attn_decode_workspace_bytes(8, 8, 2048) == 8 * 64 * 8 * 2048 + 8 * 64 * 8 * 4
     # batch 512 x 2048 slots: 128 tiles need 16 ranges of 8
     assert sa.sparse_attn_decode_workspace_bytes(512, 1, 2048) == 512 * 16 * 2048 + 32768
     assert sa.sparse_attn_decode_workspace_bytes(0, 8, 2048) == 0

@@ -215,11 +215,12 @@ bool chunk_union_layout(int32_t total_q, int32_t num_reqs, int32_t topk, int32_t
 // Slot ranges of a decode launch. Range s of S takes a request's 16-slot
 // tiles s, s + S, s + 2S, ... (so a request whose valid slots come first
 // still spreads them over its ranges). S aims at kDecodeTeams (request,
-// range) teams, as many as the chip holds at once, and at most
+// range) teams, one wave per SIMD (a sweep of 256 to 4096 teams measured
+// 512 fastest: more ranges only add partial rows to merge), and at most
 // kDecodeTilesPerRange tiles per range. Workspace: normalised partial O
 // [batch * S][heads][512] fp32, then partial LSE [batch * S][heads] fp32,
 // each 256-byte aligned.
-constexpr int64_t kDecodeTeams = 1024;
+constexpr int64_t kDecodeTeams = 512;
 constexpr int64_t kDecodeTilesPerRange = 8;
 
 struct DecodeLayout {
