@@ -126,7 +126,7 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // L2), with the chunks dealt round-robin to the XCDs so every XCD gets work
 // from the whole range (rows with short visible prefixes carry less work).
 // The last, partial round of chunks is split into contiguous bands.
-constexpr int kXcdChunk = 64;
+constexpr int kXcdChunk = 32;   // of 16, 32, 64, 128, 256 measured, 32 fastest
 
 __device__ __forceinline__ int xcd_remap(int b, int nblk) {
   constexpr int X = 8;
