@@ -7,18 +7,26 @@ One step is one sparse_attn_chunk_prefill call over the 8192-row workload
 indices, 6 query heads over one KV head, head dim 256, bf16 inputs, fp32
 output and log-sum-exp), with every input already resident in HBM.
 
+Timing follows the pages' protocol: about 40 ms of untimed calls first (the
+GPU's clocks ramp up after the host has left it idle), then the warm-up
+calls, then the timed calls with a HIP event recorded after each one on the
+launch stream; the line gives the mean and the median of the per-call times.
+
 Prints one JSON line. `value` is the gathered-KV throughput: the K and V rows
 of every valid slot (8192 * 2051 * (512 + 512) B = 17.205 GB per call)
-divided by the measured time per call. `roofline.achieved` is the same
-algorithmic byte count divided by the kernel's average duration, measured
-with HIP events on the stream the kernel is launched on; it is compared with
-MI355X's 8 TB/s HBM3E peak (gathered bytes can exceed HBM traffic when rows
-repeat in cache; `roofline.traffic` holds the measured HBM bytes per call from
-rocprofv3 counters when they were taken on the current kernel source).
+divided by the measured time per call. Those bytes exceed HBM traffic many
+times over (neighbouring rows select mostly the same tokens, which then come
+from the caches), so `roofline` is taken on the vector L1 data path instead:
+`achieved` is the bytes the kernel's vector loads request per call (the K/V
+rows of every slot tile its teams issue, counted on the host from the index
+rows and the team shapes), over the kernel's mean duration; `peak` is 128 B
+per clock per CU (one cache line) x 256 CUs x 2.4 GHz. `traffic` is the HBM
+bytes per call that rocprofv3 counters measured on the current kernel
+source (null when the source has changed since).
 
-The CPU baseline runs the fp64 oracle on a bounded sample of the same
-workload's rows, in worker processes started before the GPU is touched, and
-its results double as a parity gate on those rows.
+The CPU baseline runs the fp64 oracle on every row of the same workload
+(`--cpu-stride N`: every N-th row), in worker processes forked before the
+GPU is touched, and its results double as a parity gate on those rows.
 """
 from __future__ import annotations
 
@@ -40,9 +48,13 @@ import gen  # noqa: E402
 
 METRIC = "sparse prefill ms/call + gathered-KV GB/s (% HBM roofline), 8192 rows × 2051 slots"
 HBM_PEAK_GBS = 8000.0
+# Vector L1 data cache: one 128-byte line per clock per CU (the ceiling AMD's
+# rocprofiler-compute sets for gfx950's vL1D), 256 CUs at 2.4 GHz.
+VL1D_PEAK_GBS = 256 * 128 * 2.4
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 FP8_RECORD_BYTES = 656          # one FP8 MLA record per gathered decode slot
 KERNEL_SOURCE = os.path.join(ROOT, "top_index_sparse_amd", "csrc", "sa_gqa.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gqa_d256_c1_traffic.txt")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "gqa_d256_c1_counters.txt")
 
 
 def gathered_bytes(case: gen.AttnCase) -> int:
@@ -71,17 +83,64 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes per call measured by rocprofv3 counters, if they were taken
-    on the current kernel source; else None."""
+def load_counters():
+    """The headline kernel's rocprofv3 counter summary (HBM bytes per call,
+    vector L1 bytes, unit busy fractions), if it was taken on the current
+    kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
-            kv = dict(l.split(":", 1) for l in f if ":" in l)
+        with open(COUNTER_FILE) as f:
+            kv = dict(l.split(":", 1) for l in f if ":" in l and not l.startswith("#"))
         if kv.get("kernel_source_sha256_16", "").strip() != kernel_source_hash():
             return None
-        return float(kv["hbm_bytes_per_call"])
-    except (OSError, KeyError, ValueError):
+        return {k.strip(): float(v) for k, v in kv.items() if k.strip() != "kernel_source_sha256_16"}
+    except (OSError, ValueError):
         return None
+
+
+def team_tiles(idx: np.ndarray, kv_len, rows_per_team: int, cu_q=None, cu_kv=None,
+               every_tile: bool = False):
+    """Slot tiles the per-token team kernel issues, from the index rows.
+
+    A team takes `rows_per_team` consecutive rows and walks their slots in
+    tiles of 16 positions. A position is gathered once for every row whose
+    token there equals the team's first row's; any other valid token is
+    queued, once per run of consecutive rows holding it at that position, and
+    the queue is gathered 16 tokens at a time. A tile with no valid token of
+    the first row is skipped (`every_tile`: the three-tile shape issues all).
+    Tokens are compared as global KV rows (request base + local index).
+
+    Returns (tiles issued per KV head, valid K/V rows gathered per KV head).
+    """
+    T, k = idx.shape
+    R = rows_per_team
+    nt = (k + 15) // 16
+    teams = (T + R - 1) // R
+    X = np.full((teams * R, nt * 16), -1, dtype=np.int64)
+    X[:T, :k] = idx
+    if cu_q is None:
+        ok = (X >= 0) & (X < kv_len)
+        X = np.where(ok, X, -1)
+    else:
+        req = np.searchsorted(np.asarray(cu_q), np.arange(teams * R), side="right") - 1
+        req = np.minimum(req, len(cu_q) - 2)
+        base = np.asarray(cu_kv)[req][:, None]
+        length = (np.asarray(cu_kv)[req + 1] - np.asarray(cu_kv)[req])[:, None]
+        ok = (X >= 0) & (X < length)
+        ok[T:] = False
+        X = np.where(ok, X + base, -1)
+    X = X.reshape(teams, R, nt * 16)
+    row0 = X[:, 0, :]
+    first = row0 >= 0
+    primary = teams * nt if every_tile else int(first.reshape(teams, nt, 16).any(-1).sum())
+    queued = np.zeros(teams, dtype=np.int64)
+    for r in range(1, R):
+        x = X[:, r, :]
+        start = (x >= 0) & (x != row0)
+        if r >= 2:
+            start &= x != X[:, r - 1, :]
+        queued += start.sum(-1)
+    tiles = primary + int(((queued + 15) // 16).sum())
+    return tiles, int(first.sum() + queued.sum())
 
 
 # ----------------------------------------------------------- CPU baseline
@@ -170,6 +229,19 @@ def _rate(nbytes, ms):
             "bytes": int(nbytes)}
 
 
+def _l1(r, nbytes):
+    """Adds the vector L1 bytes the kernel's loads request and their rate
+    against the vL1D ceiling to a result line."""
+    gbs = nbytes / (r["ms"] * 1e-3) / 1e9
+    r["vl1d_bytes"] = int(nbytes)
+    r["vl1d_frac"] = round(gbs / VL1D_PEAK_GBS, 4)
+    return r
+
+
+def _union_tiles(ul, teams_per_group=1):
+    return int(((ul.astype(np.int64) + 15) // 16).sum()) * teams_per_group
+
+
 def measure_others(args, sa, torch, stream):
     """Times every other workload once (HIP events on the launch stream)."""
     def bf16(a):
@@ -225,7 +297,8 @@ def measure_others(args, sa, torch, stream):
     sidx = torch.from_numpy(gen.shuffle_slots(c.idx, args.seed + 1)).cuda()
     ms = _events_ms(torch, stream, lambda: sa.sparse_attn_chunk_prefill(
         q, k, v, sidx, cu_q1, cu_kv1, sm_scale=c.scale, out=out, lse=lse, stream=stream), w, n)
-    r = _rate(per_token_bytes, ms)
+    r = _l1(_rate(per_token_bytes, ms),
+            team_tiles(gen.shuffle_slots(c.idx, args.seed + 1), c.kv_len, 2)[0] * 16 * 1024)
     ms_u = _events_ms(torch, stream, lambda: sa.sparse_attn_prefill_union(
         q, k, v, sidx, 2, sm_scale=c.scale, ws=ws, out=out, lse=lse, stream=stream), w, n)
     r.update({"union_G2_ms": round(ms_u, 4)})
@@ -270,7 +343,9 @@ def measure_others(args, sa, torch, stream):
     lse = torch.empty((c.num_rows, c.num_q_heads), dtype=torch.float32, device="cuda")
     ms = _events_ms(torch, stream, lambda: sa.sparse_attn_prefill(
         q, k, v, idx, sm_scale=c.scale, out=out, lse=lse, stream=stream), w, n)
-    res["group12_2kv_prefill"] = _rate(gathered_bytes(c), ms)
+    res["group12_2kv_prefill"] = _l1(
+        _rate(gathered_bytes(c), ms),
+        team_tiles(c.idx, c.kv_len, 4, every_tile=True)[0] * 16 * 1024 * c.num_kv_heads)
     del q, k, v, idx, out, lse
 
     # MLA per-token and union
@@ -282,7 +357,8 @@ def measure_others(args, sa, torch, stream):
     per_token_bytes = gathered_bytes(c)
     ms = _events_ms(torch, stream, lambda: sa.sparse_attn_prefill(
         q, k, None, idx, sm_scale=c.scale, head_dim_v=512, out=out, lse=lse, stream=stream), w, n)
-    res["mla_per_token"] = _rate(per_token_bytes, ms)
+    res["mla_per_token"] = _l1(_rate(per_token_bytes, ms),
+                               team_tiles(c.idx, c.kv_len, 2)[0] * 16 * 1152)
     for G in (2, 4):
         ws = torch.empty(sa.sparse_attn_union_workspace_bytes(c.num_rows, c.topk, G),
                          dtype=torch.uint8, device="cuda")
@@ -300,6 +376,11 @@ def measure_others(args, sa, torch, stream):
                   "attention_ms": round(ms_all - ms_build, 4),
                   "per_token_equivalent_GBps": round(per_token_bytes / (ms_all * 1e-3) / 1e9, 1),
                   "speedup_vs_per_token": round(res["mla_per_token"]["ms"] / ms_all, 3)})
+        # (a team serves 16 / heads members of a group and streams the whole
+        # list: G=4 over 8 heads has two teams per group)
+        tpg = -(-G // (16 // c.num_q_heads))
+        _l1(r, _union_tiles(ul.cpu().numpy(), tpg) * 16 * 1152)
+        r["vl1d_bytes_per_row_gathered"] = round(r["vl1d_bytes"] / rows, 1)
         res[f"mla_union_G{G}"] = r
         del ws, ui, ub, ul
     del q, k, idx, out, lse
@@ -334,7 +415,9 @@ def measure_others(args, sa, torch, stream):
     lse = torch.empty((c.num_rows, c.num_q_heads), dtype=torch.float32, device="cuda")
     ms = _events_ms(torch, stream, lambda: sa.sparse_attn_chunk_prefill(
         q, k, v, idx, cu_q, cu_kv, sm_scale=c.scale, out=out, lse=lse, stream=stream), w, n)
-    res["ragged_chunk_prefill"] = _rate(gathered_bytes(c), ms)
+    res["ragged_chunk_prefill"] = _l1(
+        _rate(gathered_bytes(c), ms),
+        team_tiles(c.idx, None, 2, c.cu_seqlens_q, c.cu_seqlens_kv)[0] * 16 * 1024)
     res["ragged_chunk_prefill"]["rows"] = c.num_rows
     # union mode over the same ragged requests (groups of 2 rows per request)
     ws = torch.empty(sa.sparse_attn_chunk_union_workspace_bytes(c.num_rows, len(cu_q) - 1,
@@ -498,22 +581,26 @@ def main():
         sa.sparse_attn_chunk_prefill(q, k, v, idx, cu_q, cu_kv, total_q=case.num_rows,
                                      sm_scale=case.scale, out=out, lse=lse, stream=stream)
 
+    # the pages' protocol: clocks settled, warm-up calls, then every timed
+    # call bracketed by events on the launch stream (median and mean)
+    _settle(torch, stream, step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     calls0 = sa.sa_call_count("sparse_attn_chunk_prefill")
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert sa.sa_call_count("sparse_attn_chunk_prefill") - calls0 == args.steps
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    per_call = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    kernel_ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    kernel_ms_median = float(np.median(per_call))
     ms = wall * 1e3 / args.steps
 
     parity = None
@@ -540,13 +627,20 @@ def main():
     copy_gbs = 2.0 * (1 << 30) / (copy_ms * 1e-3) / 1e9
     del csrc, cdst
 
-    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    # The vector L1 bytes the kernel's loads request: every slot tile a team
+    # issues loads 16 K rows and 16 V rows (512 B each; invalid slots read a
+    # cached row of zeros). Two rows x 6 heads share one 16-column tile.
+    tiles, rows_gathered = team_tiles(case.idx, case.kv_len, 2)
+    l1_bytes = tiles * 16 * 1024 * case.num_kv_heads
+    l1_gbs = l1_bytes / (kernel_ms * 1e-3) / 1e9
+    # Issued MFMA work per tile: S^T over 8 k-steps of 16x16x32 and O^T over
+    # 16 d-blocks of 16x16x16, one 16-column tile.
+    mfma_flops = tiles * (8 * 2 * 16 * 16 * 32 + 16 * 2 * 16 * 16 * 16)
     valid_slots = nbytes // 1024
     tflops = 2.0 * case.num_q_heads * valid_slots * (case.head_dim_qk + case.head_dim_v) \
         / (kernel_ms * 1e-3) / 1e12
-    # The MFMA products run on 16-column tiles: two rows x 6 heads fill 12 of
-    # the 16 columns, so the issued work is 16/12 of the useful work.
-    tflops_issued = tflops * 16.0 / 12.0
+    counters = load_counters()
+    traffic = counters.get("hbm_bytes_per_call") if counters else None
     result = {
         "metric": METRIC,
         "value": round(nbytes / (ms * 1e-3) / 1e9, 1),
@@ -570,15 +664,22 @@ def main():
             "gathered_bytes_per_call": nbytes,
         },
         "roofline": {
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(),
+            "bound": "vl1d", "achieved": round(l1_gbs, 1), "peak": round(VL1D_PEAK_GBS, 1),
+            "unit": "GB/s", "frac": round(l1_gbs / VL1D_PEAK_GBS, 4), "traffic": traffic,
+            "bytes_per_call": l1_bytes, "tiles_per_call": tiles,
+            "valid_rows_gathered_per_call": rows_gathered,
+            "hbm_frac": (round(traffic / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                         if traffic else None),
+            "mfma_issued_frac": round(mfma_flops / (kernel_ms * 1e-3) / 1e12
+                                      / MFMA_BF16_PEAK_TFLOPS, 4),
         },
         "cpu_baseline": cpu,
         "kernel_ms": round(kernel_ms, 4),
+        "kernel_ms_median": round(kernel_ms_median, 4),
+        "gathered_frac_hbm_peak": round(nbytes / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "tflops_useful": round(tflops, 2),
-        "mfma_frac_issued": round(tflops_issued / 2500.0, 4),
         "copy_probe_GBps": round(copy_gbs, 1),
-        "frac_of_copy_probe": round(achieved / copy_gbs, 4),
+        "counters": counters,
         "parity": parity,
         "others": others,
     }

@@ -11,6 +11,16 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+    # The every-row parity tests evaluate the oracle in worker processes
+    # forked from a forkserver; it must start before anything initialises the
+    # GPU (counting devices does not).
+    try:
+        import torch
+        if torch.cuda.device_count() > 0:
+            from tests import oracle_pool
+            oracle_pool.start()
+    except Exception:
+        pass
 
 
 def pytest_collection_modifyitems(config, items):
