@@ -18,11 +18,11 @@ For row t of a request whose KV buffer holds kv_len tokens, and head h:
 Readings where the pages are silent:
 
 * An index outside [0, kv_len) is masked like -1 (the pages' tests cover
-  "negative and out-of-range selected indices" without stating the
+  negative and out-of-range selected indices without stating the
   semantics; the library never dereferences such a slot).
 * An empty support gives O = 0 and LSE = -inf.
 * A duplicated index counts with its multiplicity (PR 32779, "Accuracy
-  Tests": a duplicated row is weighted twice on the per-token path).
+  Tests": on the per-token path a row selected twice counts twice).
 * MLA latent rows: V is the first Dv columns of the K row (PR 32779, "Speed
   Tests": 576-wide rows, 512 used as V).
 * No causal mask beyond the index set: the indexer owns causality.
@@ -121,7 +121,8 @@ def chunk_prefill(q: np.ndarray, k: np.ndarray, v: Optional[np.ndarray],
                   *, num_kv_heads: int, scale: float, head_dim_v: Optional[int] = None,
                   rows: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Ragged chunk prefill (PR 37275, "Kernel measurements": the chunk kernel
-    serves prefill with a cached prefix and every chunk after the first).
+    runs when a prompt continues a cached prefix, i.e. for each chunk past
+    the first).
 
     Request r owns query rows [cu_seqlens_q[r], cu_seqlens_q[r+1]) and the KV
     tokens [cu_seqlens_kv[r], cu_seqlens_kv[r+1]) of the packed K/V buffers;

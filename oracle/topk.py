@@ -1,10 +1,9 @@
 """Indexer top-k selection (TEST INFRASTRUCTURE: oracle only).
 
-sglang PR 37275, "Motivation": for every query row the indexer selects
-token_topk + compress_ratio - 1 = 2051 token slots, and the attention kernel
-streams up to that budget, fewer where the row's visible context is shorter;
-"Not covered": the scoring and selection chain feeds the sparse kernels
-unchanged. The scoring needs trained weights and stays outside; what is
+sglang PR 37275, "Motivation": the indexer gives every query row a budget
+of 2051 token slots (its top-k plus the compression ratio, minus one), and
+a row that sees fewer tokens than that uses fewer slots; "Not covered": the
+sparse kernels take the selected rows as they come. The scoring needs trained weights and stays outside; what is
 restated here is the selection, from given fp32 scores to the int32 index
 rows the attention entry points take.
 
@@ -17,7 +16,7 @@ scores; n_t = kv_len when no lengths are given):
                 idx[t] = S_t in ascending order
 
 Readings (the pages name the selection but not its tie rule, its output
-order or its padding beyond "streams less"):
+order or its padding beyond shorter rows using fewer slots):
 
 * Ties in value go to the lower position; -0.0 and +0.0 are equal values
   (plain float comparison). Scores are never NaN.

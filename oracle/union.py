@@ -4,10 +4,11 @@ oracle only).
 sglang PR 32779, "Modifications" (``--dsa-triton-union``): G adjacent tokens
 share one gathered index set; a per-row ownership bitmask restores each
 token's own softmax support, so the result equals the per-token path. The set
-is built per group: each token's rows are sorted on their own, then a token
-emits a row if no earlier token of the group selected it, and every token
-that selected a row sets its bit. The accuracy section adds the contract:
-each row once, bits equal to the OR of its owners, -1 dropped.
+is built per group: each token's rows are sorted on their own; a row goes
+into the set under the first token of the group that holds it, and its bits
+mark every token of the group that holds it. "Accuracy Tests" states the
+contract the tests check: no row appears twice, a row's bits are the union
+of its holders' bits, and -1 slots are left out.
 
 Canonical layout (the pages fix the membership, not the storage; this is the
 reading the library follows):

@@ -1,4 +1,4 @@
-// Sparse GQA prefill kernels, head dim 256 (K and V separate, group <= 16):
+// Sparse GQA prefill kernels, head dim 256 (K and V separate, group <= 32):
 // per-token (one request or ragged requests) and union instantiations of
 // attn_kernel, for three team shapes.
 #include "sa_attn_kernel.h"
