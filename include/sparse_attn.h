@@ -16,8 +16,10 @@
  *
  * Conventions for every entry point:
  *   - Device pointers are owned by the caller. The library allocates and
- *     frees nothing, keeps no state between calls except call counters and
- *     the last error message, and never reads device memory from the host.
+ *     frees nothing, keeps no state between calls except call counters, the
+ *     last error message and the static decode scratch of
+ *     sparse_attn_decode_paged_noalloc, and never reads device memory from
+ *     the host.
  *   - Work is enqueued on `stream` and returns without synchronising; the
  *     grids depend on host scalars only, so every call can be captured in a
  *     HIP graph.
@@ -304,6 +306,33 @@ sa_status sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_page_desc*
                                    void* ws, size_t ws_bytes, float* out, float* lse,
                                    hipStream_t stream);
 
+/* Bytes of the static device scratch behind sparse_attn_decode_paged_noalloc
+ * (each GPU the library runs on holds its own copy until the process ends). */
+#define SA_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* sparse_attn_decode_paged without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). Same arguments, results
+ * and errors as sparse_attn_decode_paged, which it shares its kernels with;
+ * the partial results live in a static device array of
+ * SA_DECODE_SCRATCH_BYTES per GPU instead of `ws`.
+ *
+ * A call whose sparse_attn_decode_workspace_bytes(batch, num_q_heads, topk)
+ * exceeds SA_DECODE_SCRATCH_BYTES returns SA_ERR_WORKSPACE before anything
+ * is launched (at topk 2048 a request head takes 16 ranges of 2052 bytes,
+ * so batch x num_q_heads up to 1022 fits). The first call on a device looks
+ * up that device's scratch address (SA_ERR_HIP if the runtime refuses).
+ * Calls on one GPU share its scratch, which keeps the last call's contents:
+ * calls that overlap on one GPU (different streams, or different threads)
+ * race and must be serialised by the caller. Nothing is allocated or freed;
+ * no memset is enqueued.
+ */
+sa_status sparse_attn_decode_paged_noalloc(const sa_attn_desc* desc, const sa_page_desc* pages,
+                                           const void* q, const uint8_t* pool,
+                                           int32_t num_dst_pages, const int32_t* idx,
+                                           const int32_t* topk_len, int32_t batch, float* out,
+                                           float* lse, hipStream_t stream);
+
 /* Indexer top-k selection (sglang PR 37275, "Motivation": the indexer
  * selects token_topk + compress_ratio - 1 = 2051 token slots per query row,
  * fewer where the row's visible context is shorter). Row t keeps the k
@@ -345,7 +374,8 @@ typedef enum {
   SA_ENTRY_CHUNK_PREFILL_UNION = 6,
   SA_ENTRY_DECODE_PAGED = 7,
   SA_ENTRY_INDEXER_TOPK = 8,
-  SA_ENTRY_COUNT = 9
+  SA_ENTRY_DECODE_PAGED_NOALLOC = 9,
+  SA_ENTRY_COUNT = 10
 } sa_entry;
 uint64_t sa_call_count(int32_t entry);
 

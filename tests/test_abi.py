@@ -27,6 +27,7 @@ def test_header_declares_the_entry_points():
     for want in ("sparse_attn_prefill", "sparse_attn_chunk_prefill", "sparse_attn_prefill_union",
                  "sparse_attn_union_build", "sparse_attn_union_workspace_bytes", "page_mark",
                  "page_split", "sparse_attn_decode_paged", "sparse_attn_decode_workspace_bytes",
+                 "sparse_attn_decode_paged_noalloc",
                  "indexer_topk",
                  "sa_validate_attn", "sa_last_error", "sa_call_count"):
         assert want in names
@@ -306,6 +307,32 @@ def test_decode_rejects_on_host():
     before = sa.sa_call_count("sparse_attn_decode_paged")
     assert call(batch=0, w=None, wb=0) == 0                         # nothing to launch, counted
     assert sa.sa_call_count("sparse_attn_decode_paged") == before + 1
+
+
+def test_decode_noalloc_rejects_on_host():
+    # the same validation as the workspace entry point, then the size check
+    # against the static scratch, all before the scratch is looked up
+    f = sa.lib().sparse_attn_decode_paged_noalloc
+    fp8 = _mla(kv_dtype=sa.SA_DTYPE_FP8_E4M3, kv_row_stride=656)
+    pg = sa.PageDesc(src_page_tokens=256, dst_page_tokens=64, row_bytes=656, scale_bytes=4,
+                     src_page_stride=256 * 660, dst_page_stride=64 * 660)
+
+    def call(d=fp8, p=pg, batch=32, pool=0x2000):
+        return f(None if d is None else ctypes.byref(d), None if p is None else ctypes.byref(p),
+                 0x1000, pool, 16384, 0x3000, None, batch, 0x4000, 0x5000, None)
+
+    assert call(d=None) == -1
+    assert call(d=_mla()) == -3                                     # bf16 rows
+    assert call(p=None) == -1
+    assert call(pool=None) == -1
+    assert call(batch=-1) == -2
+    # batch x heads beyond the scratch (16 ranges x 2052 B per request head)
+    assert sa.sparse_attn_decode_workspace_bytes(128, 8, 2048) > sa.SA_DECODE_SCRATCH_BYTES
+    assert call(batch=128) == -5
+    assert "static scratch" in sa.sa_last_error()
+    before = sa.sa_call_count("sparse_attn_decode_paged_noalloc")
+    assert call(batch=0) == 0                                       # nothing to launch, counted
+    assert sa.sa_call_count("sparse_attn_decode_paged_noalloc") == before + 1
 
 
 def test_indexer_topk_rejects_on_host():

@@ -30,6 +30,7 @@ __all__ = [
     "page_split",
     "sparse_attn_decode_workspace_bytes",
     "sparse_attn_decode_paged",
+    "sparse_attn_decode_paged_noalloc",
     "indexer_topk",
     "sa_validate_attn",
     "sa_last_error",
@@ -52,7 +53,9 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_OK_FALLBACK", -1: "SA_ERR_NULL", -2: "SA_ERR_
 ENTRIES = {"sparse_attn_prefill": 0, "sparse_attn_chunk_prefill": 1,
            "sparse_attn_union_build": 2, "sparse_attn_prefill_union": 3,
            "page_mark": 4, "page_split": 5, "sparse_attn_chunk_prefill_union": 6,
-           "sparse_attn_decode_paged": 7, "indexer_topk": 8}
+           "sparse_attn_decode_paged": 7, "indexer_topk": 8,
+           "sparse_attn_decode_paged_noalloc": 9}
+SA_DECODE_SCRATCH_BYTES = 32 << 20
 
 
 class SparseAttnError(RuntimeError):
@@ -111,6 +114,8 @@ _SIGNATURES = {
     "indexer_topk": (_I32, [_P, _I64, _P, _I32, _I32, _I32, _P, _I64, _P]),
     "sparse_attn_decode_paged": (_I32, [ctypes.POINTER(AttnDesc), ctypes.POINTER(PageDesc), _P, _P,
                                         _I32, _P, _P, _I32, _P, _SZ, _P, _P, _P]),
+    "sparse_attn_decode_paged_noalloc": (_I32, [ctypes.POINTER(AttnDesc), ctypes.POINTER(PageDesc),
+                                                _P, _P, _I32, _P, _P, _I32, _P, _P, _P]),
     "sa_validate_attn": (ctypes.c_int, [ctypes.POINTER(AttnDesc), _I32]),
     "sa_last_error": (ctypes.c_char_p, []),
     "sa_call_count": (ctypes.c_uint64, [_I32]),
@@ -468,21 +473,8 @@ def sparse_attn_decode_workspace_bytes(batch: int, num_q_heads: int, topk: int) 
     return int(lib().sparse_attn_decode_workspace_bytes(batch, num_q_heads, topk))
 
 
-def sparse_attn_decode_paged(q: torch.Tensor, pool: torch.Tensor, idx: torch.Tensor, *,
-                             dst_page_tokens: int = 64, scale_bytes: int = 4,
-                             sm_scale: Optional[float] = None,
-                             topk_len: Optional[torch.Tensor] = None,
-                             ws: Optional[torch.Tensor] = None,
-                             out: Optional[torch.Tensor] = None,
-                             lse: Optional[torch.Tensor] = None,
-                             stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Sparse MLA decode over the split pool (C: sparse_attn_decode_paged).
-
-    q [B, Hq, 576] bf16 (one query row per request); pool uint8
-    [num_dst_pages, dst_page_stride] (pages of dst_page_tokens 656-byte FP8
-    records, then their per-token words); idx [B, topk] int32 pool token ids;
-    topk_len optional [B] int32. Returns (out [B, Hq, 512] fp32, lse [B, Hq]).
-    """
+def _decode_prep(q, pool, idx, dst_page_tokens, scale_bytes, sm_scale, topk_len, out, lse,
+                 allocate):
     _need(q, "q", torch.bfloat16, 3)
     _need(pool, "pool", torch.uint8, 2, q.device)
     _need(idx, "idx", torch.int32, 2, q.device)
@@ -500,10 +492,12 @@ def sparse_attn_decode_paged(q: torch.Tensor, pool: torch.Tensor, idx: torch.Ten
             raise ValueError("topk_len must be a contiguous [B] tensor")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[2])
-    if out is None:
+    if allocate and out is None:
         out = torch.empty((B, Hq, 512), dtype=torch.float32, device=q.device)
-    if lse is None:
+    if allocate and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if out is None or lse is None:
+        raise ValueError("out and lse must be given")
     _need(out, "out", torch.float32, 3, q.device)
     _need(lse, "lse", torch.float32, 2, q.device)
     _need_size(out, "out", B, (Hq, 512))
@@ -519,13 +513,52 @@ def sparse_attn_decode_paged(q: torch.Tensor, pool: torch.Tensor, idx: torch.Ten
     pages = PageDesc(src_page_tokens=0, dst_page_tokens=dst_page_tokens,
                      row_bytes=FP8_RECORD_BYTES, scale_bytes=scale_bytes, src_page_stride=0,
                      dst_page_stride=pool.stride(0))
-    nbytes = sparse_attn_decode_workspace_bytes(B, Hq, idx.shape[1])
+    return desc, pages, out, lse, B
+
+
+def sparse_attn_decode_paged(q: torch.Tensor, pool: torch.Tensor, idx: torch.Tensor, *,
+                             dst_page_tokens: int = 64, scale_bytes: int = 4,
+                             sm_scale: Optional[float] = None,
+                             topk_len: Optional[torch.Tensor] = None,
+                             ws: Optional[torch.Tensor] = None,
+                             out: Optional[torch.Tensor] = None,
+                             lse: Optional[torch.Tensor] = None,
+                             stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Sparse MLA decode over the split pool (C: sparse_attn_decode_paged).
+
+    q [B, Hq, 576] bf16 (one query row per request); pool uint8
+    [num_dst_pages, dst_page_stride] (pages of dst_page_tokens 656-byte FP8
+    records, then their per-token words); idx [B, topk] int32 pool token ids;
+    topk_len optional [B] int32. Returns (out [B, Hq, 512] fp32, lse [B, Hq]).
+    """
+    desc, pages, out, lse, B = _decode_prep(q, pool, idx, dst_page_tokens, scale_bytes,
+                                            sm_scale, topk_len, out, lse, True)
+    nbytes = sparse_attn_decode_workspace_bytes(B, desc.num_q_heads, idx.shape[1])
     ws = _workspace(ws, nbytes, q.device) if B > 0 else ws
     st = lib().sparse_attn_decode_paged(ctypes.byref(desc), ctypes.byref(pages), _ptr(q),
                                         _ptr(pool), pool.shape[0], _ptr(idx), _ptr(topk_len), B,
                                         _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                         _ptr(out), _ptr(lse), _stream(stream))
     _check(st, "sparse_attn_decode_paged")
+    return out, lse
+
+
+def sparse_attn_decode_paged_noalloc(q: torch.Tensor, pool: torch.Tensor, idx: torch.Tensor, *,
+                                     out: torch.Tensor, lse: torch.Tensor,
+                                     dst_page_tokens: int = 64, scale_bytes: int = 4,
+                                     sm_scale: Optional[float] = None,
+                                     topk_len: Optional[torch.Tensor] = None,
+                                     stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Sparse MLA decode with the library's static scratch instead of a
+    workspace (C: sparse_attn_decode_paged_noalloc); the caller passes out
+    and lse, and nothing is allocated. Calls that overlap on one GPU race."""
+    desc, pages, out, lse, B = _decode_prep(q, pool, idx, dst_page_tokens, scale_bytes,
+                                            sm_scale, topk_len, out, lse, False)
+    st = lib().sparse_attn_decode_paged_noalloc(ctypes.byref(desc), ctypes.byref(pages), _ptr(q),
+                                                _ptr(pool), pool.shape[0], _ptr(idx),
+                                                _ptr(topk_len), B, _ptr(out), _ptr(lse),
+                                                _stream(stream))
+    _check(st, "sparse_attn_decode_paged_noalloc")
     return out, lse
 
 

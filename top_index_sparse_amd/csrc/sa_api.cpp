@@ -481,12 +481,20 @@ size_t sparse_attn_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, in
   return (size_t)L.total;
 }
 
-sa_status sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_page_desc* pages,
-                                   const void* q, const uint8_t* pool, int32_t num_dst_pages,
-                                   const int32_t* idx, const int32_t* topk_len, int32_t batch,
-                                   void* ws, size_t ws_bytes, float* out, float* lse,
-                                   hipStream_t stream) {
-  g_err[0] = 0;
+}  // extern "C"
+
+namespace sa {
+
+// The decode entry points' common body: validation, then the range teams
+// and the merge over the workspace: the caller's `ws`, or, when `scratch`
+// is given, the static scratch of `ws_bytes` it returns once every argument
+// has passed (nullptr, with a message, when its lookup fails). Counts a
+// successful call under `entry`.
+sa_status decode_paged_ws(const sa_attn_desc* desc, const sa_page_desc* pages, const void* q,
+                          const uint8_t* pool, int32_t num_dst_pages, const int32_t* idx,
+                          const int32_t* topk_len, int32_t batch, void* ws, size_t ws_bytes,
+                          float* out, float* lse, hipStream_t stream, int entry,
+                          ScratchFn scratch) {
   Kernel kernel = Kernel::kNone;
   sa_status st = check_desc(desc, 1, &kernel);
   if (st != SA_OK) return st;
@@ -518,9 +526,19 @@ sa_status sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_page_desc*
   if (!decode_layout(batch, desc->num_q_heads, desc->topk, &L))
     return fail(SA_ERR_SHAPE, "decode of batch %d x topk %d does not fit one launch", batch,
                 desc->topk);
-  if (batch == 0) return ok(SA_ENTRY_DECODE_PAGED);
+  if (batch == 0) return ok(static_cast<sa_entry>(entry));
   st = check_ptrs(desc, q, pool, nullptr, idx, out, lse);
   if (st != SA_OK) return st;
+  if (scratch) {
+    if ((size_t)L.total > ws_bytes)
+      return fail(SA_ERR_WORKSPACE,
+                  "decode of batch %d x %d heads x topk %d needs %lld bytes of partial results; "
+                  "the static scratch holds %zu (use sparse_attn_decode_paged with a workspace)",
+                  batch, desc->num_q_heads, desc->topk, (long long)L.total, ws_bytes);
+    char msg[200] = "";
+    ws = scratch(msg, sizeof(msg));
+    if (!ws) return fail(SA_ERR_HIP, "%s", msg);
+  }
   if (!ws || ws_bytes < (size_t)L.total || (reinterpret_cast<uintptr_t>(ws) & 255u))
     return fail(SA_ERR_WORKSPACE, "ws: needs %lld bytes, 256-byte aligned (got %zu)",
                 (long long)L.total, ws_bytes);
@@ -550,7 +568,23 @@ sa_status sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_page_desc*
   if (e == hipErrorInvalidConfiguration)
     return fail(SA_ERR_SHAPE, "decode of batch %d does not fit one launch", batch);
   if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
-  return ok(SA_ENTRY_DECODE_PAGED);
+  return ok(static_cast<sa_entry>(entry));
+}
+
+void api_clear_error() { g_err[0] = 0; }
+
+}  // namespace sa
+
+extern "C" {
+
+sa_status sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_page_desc* pages,
+                                   const void* q, const uint8_t* pool, int32_t num_dst_pages,
+                                   const int32_t* idx, const int32_t* topk_len, int32_t batch,
+                                   void* ws, size_t ws_bytes, float* out, float* lse,
+                                   hipStream_t stream) {
+  g_err[0] = 0;
+  return sa::decode_paged_ws(desc, pages, q, pool, num_dst_pages, idx, topk_len, batch, ws,
+                             ws_bytes, out, lse, stream, SA_ENTRY_DECODE_PAGED, nullptr);
 }
 
 sa_status indexer_topk(const float* scores, int64_t score_row_stride, const int32_t* row_len,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sparse_attn.h"
+
 namespace sa {
 
 // One attention launch. Pointers are device pointers; strides in elements.
@@ -151,5 +153,19 @@ hipError_t launch_page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src
                             int32_t src_page_tokens, int8_t* mask, hipStream_t stream);
 hipError_t launch_page_split(const PageParams& p, hipStream_t stream);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
+
+// sa_api.cpp: the decode entry points' common body (counted under `entry`
+// on success). Without `scratch` it runs over the caller's `ws`; with it,
+// once every argument has passed, over the static scratch of `ws_bytes`
+// that scratch() returns (nullptr and a message in msg when the lookup
+// fails).
+using ScratchFn = void* (*)(char* msg, size_t msg_len);
+sa_status decode_paged_ws(const sa_attn_desc* desc, const sa_page_desc* pages, const void* q,
+                          const uint8_t* pool, int32_t num_dst_pages, const int32_t* idx,
+                          const int32_t* topk_len, int32_t batch, void* ws, size_t ws_bytes,
+                          float* out, float* lse, hipStream_t stream, int entry,
+                          ScratchFn scratch);
+// Clears the calling thread's error text (entry points defined elsewhere).
+void api_clear_error();
 
 }  // namespace sa
