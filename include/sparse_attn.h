@@ -33,8 +33,8 @@
  *     request). Invalid slots are never dereferenced and contribute nothing.
  *     A row with no valid slot gets O = 0 and LSE = -inf.
  *   - Duplicated indices in one row count with multiplicity on the
- *     per-token paths (sglang PR 32779, "Accuracy Tests": a duplicated row
- *     is weighted twice); union mode deduplicates them (each row once).
+ *     per-token paths (sglang PR 32779, "Accuracy Tests": a row selected
+ *     twice counts twice there); union mode lists every row once.
  */
 #ifndef SPARSE_ATTN_H
 #define SPARSE_ATTN_H
@@ -134,8 +134,8 @@ sa_status sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const voi
                               hipStream_t stream);
 
 /* Ragged chunk prefill (sglang PR 37275, "Kernel measurements": the chunk
- * kernel serves prefill with a cached prefix and every chunk after the
- * first). Request r owns query rows [cu_seqlens_q[r], cu_seqlens_q[r+1]) and
+ * kernel runs when a prompt continues a cached prefix, i.e. for each chunk
+ * past the first). Request r owns query rows [cu_seqlens_q[r], cu_seqlens_q[r+1]) and
  * KV tokens [cu_seqlens_kv[r], cu_seqlens_kv[r+1]) of the packed k/v; its
  * indices are local to that range.
  *
@@ -333,9 +333,9 @@ sa_status sparse_attn_decode_paged_noalloc(const sa_attn_desc* desc, const sa_pa
                                            const int32_t* topk_len, int32_t batch, float* out,
                                            float* lse, hipStream_t stream);
 
-/* Indexer top-k selection (sglang PR 37275, "Motivation": the indexer
- * selects token_topk + compress_ratio - 1 = 2051 token slots per query row,
- * fewer where the row's visible context is shorter). Row t keeps the k
+/* Indexer top-k selection (sglang PR 37275, "Motivation": each query row
+ * gets a budget of 2051 token slots, its top-k plus the compression ratio
+ * minus one, and fewer when it sees fewer tokens). Row t keeps the k
  * largest of its first n_t scores, n_t = row_len[t] clamped to [0, kv_len]
  * (kv_len when row_len is NULL); a larger score wins, equal scores go to the
  * lower position, and -0 ties with +0. The kept positions are written to
