@@ -19,8 +19,9 @@ times over (neighbouring rows select mostly the same tokens, which then come
 from the caches), so `roofline` is taken on the vector L1 data path instead:
 `achieved` is the bytes the kernel's vector loads request per call (the K/V
 rows of every slot tile its teams issue, counted on the host from the index
-rows and the team shapes), over the kernel's mean duration; `peak` is 128 B
-per clock per CU (one cache line) x 256 CUs x 2.4 GHz. `traffic` is the HBM
+rows and the team shapes), over the kernel's mean duration; `peak` is one
+L1 tag access per clock per CU, 64 B each for these loads, x 256 CUs x
+2.4 GHz. `traffic` is the HBM
 bytes per call that rocprofv3 counters measured on the current kernel
 source (null when the source has changed since).
 
@@ -48,9 +49,12 @@ import gen  # noqa: E402
 
 METRIC = "sparse prefill ms/call + gathered-KV GB/s (% HBM roofline), 8192 rows × 2051 slots"
 HBM_PEAK_GBS = 8000.0
-# Vector L1 data cache: one 128-byte line per clock per CU (the ceiling AMD's
-# rocprofiler-compute sets for gfx950's vL1D), 256 CUs at 2.4 GHz.
-VL1D_PEAK_GBS = 256 * 128 * 2.4
+# Vector L1 data cache: one tag access per clock per CU (the ceiling AMD's
+# rocprofiler-compute sets for gfx950's vL1D). The gathers' 16-byte lanes
+# take one access per 64 bytes (TCP_TOTAL_CACHE_ACCESSES counts 16 per
+# 1 KB load instruction), so their ceiling is 64 B per clock per CU:
+# 256 CUs x 64 B x 2.4 GHz.
+VL1D_PEAK_GBS = 256 * 64 * 2.4
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 FP8_RECORD_BYTES = 656          # one FP8 MLA record per gathered decode slot
 KERNEL_SOURCE = os.path.join(ROOT, "top_index_sparse_amd", "csrc", "sa_gqa.hip")

@@ -72,17 +72,29 @@
 namespace sa {
 
 // kRows: per-token results (one request, or ragged requests when cu_q is
-// set), rows grouped into teams by position. kUnion: prebuilt union lists.
-// kDecode: one team per (request, slot range) over paged FP8 records, each
-// writing that range's normalised result for a later merge; range s of S
-// takes the request's slot tiles s, s + S, s + 2S, ...
-enum : int { kRows = 0, kUnion = 1, kDecode = 2 };
+// set), rows grouped into teams by position. kRowsMember: the same for
+// two-row one-wave teams, which match their rows' tokens by membership
+// (LDS bitmaps of each row's set) instead of by slot position wherever the
+// team qualifies (see below), and by position elsewhere. kUnion: prebuilt
+// union lists. kDecode: one team per (request, slot range) over paged FP8
+// records, each writing that range's normalised result for a later merge;
+// range s of S takes the request's slot tiles s, s + S, s + 2S, ...
+enum : int { kRows = 0, kUnion = 1, kDecode = 2, kRowsMember = 3 };
+
+// Membership bitmaps: one bit per token of the team's request, one bitmap
+// per row, per wavefront; requests longer than this match by position.
+constexpr int kMemberTokens = 32768;
+constexpr int kMemberWords = kMemberTokens / 32;
 
 // Headroom of the running max in log2 units: probabilities stay <= 2^kSlack.
 constexpr float kSlack = 8.f;
 // Queued tokens per wavefront: fewer than 16 wait between tiles and one
 // slot tile adds at most 3 x 16.
 constexpr int kQueueCap = 64;
+// Membership teams queue their whole token list, a chunk of bitmap words at
+// a time: fewer than 16 wait when a chunk is appended, and a chunk stops
+// before it would overflow.
+constexpr int kMemberQueueCap = 256;
 
 template <int DQK, int DV, bool V_IN_K, int MODE, int C, int WSPLIT, bool FP8>
 struct AttnTile {
@@ -107,6 +119,7 @@ struct AttnTile {
   // block scales, 64 bf16 rope values), dequantised into the same bf16 slice
   static_assert(!FP8 || (VKLDS && DQK == 576 && DV == 512 && WSPLIT == 2), "FP8 records");
   static_assert(MODE != kDecode || (FP8 && C == 1), "decode reads paged FP8 records, one row per team");
+  static_assert(MODE != kRowsMember || (WSPLIT == 1 && !V_IN_K), "membership: one-wave GQA teams");
   static constexpr int KCH = KLDS ? KSTEPS / 4 : 0;   // 16-byte K chunks per slot per lane
   static constexpr int KROW = 64 * KSTEPS + 16;       // LDS row pitch (bytes): 16 (mod 32) * odd
   static constexpr int KLDS_BYTES = 16 * KROW;
@@ -130,13 +143,14 @@ static __device__ __attribute__((aligned(16))) uint8_t kZeroRow[2048];
 template <int DQK, int DV, bool V_IN_K, int MODE, int C, int WSPLIT, bool FP8>
 __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int split,
                                           f32x4_t* xch, uint8_t* klds, int32_t* qtok_all,
-                                          uint32_t* qbits_all) {
+                                          uint32_t* qbits_all, uint32_t* bmap_all) {
   using TT = AttnTile<DQK, DV, V_IN_K, MODE, C, WSPLIT, FP8>;
   constexpr int KSTEPS = TT::KSTEPS;
   constexpr int VCH = TT::VCH;
   constexpr int MTILES = TT::MTILES;
   constexpr bool UNION = TT::UNION;
   constexpr bool DECODE = MODE == kDecode;
+  constexpr bool MEMBER = MODE == kRowsMember;
   constexpr bool VKLDS = TT::VKLDS;
   constexpr int KCH = TT::KCH;
   constexpr int KROW = TT::KROW;
@@ -250,6 +264,57 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     jm = max(jm, __builtin_amdgcn_mov_dpp(jm, 0x4e, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
     jmax = __builtin_amdgcn_readfirstlane(jm);
   }
+
+  // ---- membership (two-row teams): each row's token set as an LDS bitmap --
+  // A team qualifies when both rows exist, share one request of at most
+  // kMemberTokens tokens and hold no token twice. It then streams the union
+  // of its rows' sets in ascending token order, read off the two bitmaps,
+  // each token with the bits of the rows that hold it: each row sees each of
+  // its tokens once whatever its slot order, and neighbouring teams sweep the
+  // KV rows in the same order (their gathers meet in the caches). Otherwise
+  // the team matches its rows by slot position.
+  bool member = false;
+  uint32_t* bmp = nullptr;
+  int member_words = 0, member_base = 0;
+  if constexpr (MEMBER) {
+    bmp = bmap_all + wv * 2 * kMemberWords;
+    const int b0 = __builtin_amdgcn_readlane(base_l, 0), b1 = __builtin_amdgcn_readlane(base_l, 1);
+    const int n0 = __builtin_amdgcn_readlane(len_l, 0), n1 = __builtin_amdgcn_readlane(len_l, 1);
+    if (rows == 2 && b0 == b1 && n0 == n1 && n0 <= kMemberTokens) {
+      member_words = (n0 + 31) >> 5;
+      member_base = b0;
+      for (int w = lane; w < 2 * kMemberWords; w += 64) {
+        const int r = w >= kMemberWords;
+        if (w - r * kMemberWords < member_words) bmp[w] = 0u;
+      }
+      uint32_t dup = 0;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int jr = __builtin_amdgcn_readlane(jmax_l, r);
+        const int32_t* ir = p.idx + (int64_t)(t0 + r) * p.idx_row_stride;
+        uint32_t* br = bmp + r * kMemberWords;
+        // all of a row's index loads are issued before its marks
+        constexpr int kBatch = 36;
+        for (int j0 = 0; j0 < jr; j0 += kBatch * 64) {
+          int x[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const int j = j0 + 64 * u + lane;
+            x[u] = j < jr ? ir[j] : -1;
+          }
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            if ((unsigned)x[u] < (unsigned)n0) {
+              const uint32_t bit = 1u << (x[u] & 31);
+              dup |= atomicOr(br + (x[u] >> 5), bit) & bit;
+            }
+          }
+        }
+      }
+      member = __ballot(dup != 0u) == 0;
+    }
+  }
+
   const uint32_t team_bits = ((1u << rows) - 1u) << bit0;
   const int tiles_all = (jmax + TILE - 1) / TILE;
   const int ntiles = tiles_all > tile_first ? (tiles_all - tile_first + tile_step - 1) / tile_step : 0;
@@ -302,8 +367,9 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   };
 
   // The queue of tokens still to gather (per wave, in LDS).
-  int32_t* qtok = qtok_all + wv * kQueueCap;
-  uint32_t* qbits = qbits_all + wv * kQueueCap;
+  constexpr int QCAP = MEMBER ? kMemberQueueCap : kQueueCap;
+  int32_t* qtok = qtok_all + wv * QCAP;
+  uint32_t* qbits = qbits_all + wv * QCAP;
   int qcount = 0;
 
   // A tile to gather, as seen by an index lane: the token of slot slot_l
@@ -568,11 +634,66 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     }
   };
 
+  if (MEMBER && member) {
+    // The union of the two rows' sets, ascending: lane l takes bitmap word
+    // cw + l of a chunk and appends its tokens (with their rows' bits) at
+    // its prefix-sum offset; lanes past the queue's room wait for the next
+    // chunk. Whole tiles of 16 are consumed from the queue head; the rest
+    // (fewer than 16) move to the front before the next chunk.
+    int cw = 0;
+    while (cw < member_words || qcount > 0) {
+      if (cw < member_words) {
+        const int w = cw + lane;
+        const uint32_t m0 = w < member_words ? bmp[w] : 0u;
+        const uint32_t m1 = w < member_words ? bmp[kMemberWords + w] : 0u;
+        const uint32_t u = m0 | m1;
+        const uint32_t cnt = __popc(u);
+        const uint32_t incl = wave_scan64(cnt);
+        const bool fits = (int)incl <= QCAP - qcount && w < member_words;
+        const uint64_t fb = (uint64_t)__ballot(fits);
+        const int taken = fb == ~0ull ? 64 : __builtin_ctzll(~fb);   // a prefix of the lanes
+        if (lane < taken) {
+          int at = qcount + (int)(incl - cnt);
+          uint32_t v = u;
+          const int tok0 = member_base + 32 * w;
+          while (v) {
+            const int b = __builtin_ctz(v);
+            qtok[at] = tok0 + b;
+            qbits[at] = ((m0 >> b) & 1u) | (((m1 >> b) & 1u) << 1);
+            ++at;
+            v &= v - 1u;
+          }
+        }
+        qcount += __builtin_amdgcn_readlane((int)incl, taken - 1);
+        cw += taken;
+      }
+      const bool last = cw >= member_words;
+      int head = 0;
+      while (qcount - head >= 16 || (last && qcount - head > 0)) {
+        const bool have = slot_l < qcount - head;
+        const Tile tl{have ? qtok[head + slot_l] : -1, have ? qbits[head + slot_l] : 0u};
+        uint32_t mask[C];
+        load_data(db, tl, mask);
+        compute(db, mask);
+        head += 16;
+      }
+      const int rem = qcount > head ? qcount - head : 0;
+      if (head > 0 && rem > 0) {
+        const int vt = lane < rem ? qtok[head + lane] : 0;
+        const uint32_t vb = lane < rem ? qbits[head + lane] : 0u;
+        if (lane < rem) {
+          qtok[lane] = vt;
+          qbits[lane] = vb;
+        }
+      }
+      qcount = rem;
+    }
+  }
   // Main tiles: the next tile's indices load while this one is gathered and
   // consumed (loads retire in issue order, so they are issued first).
   Idx ib[2];
-  if (ntiles > 0) load_idx(ib[0], tile_first * TILE);
-  for (int tile = 0; tile < ntiles; tile += 2) {
+  if (!(MEMBER && member) && ntiles > 0) load_idx(ib[0], tile_first * TILE);
+  for (int tile = 0; tile < (MEMBER && member ? 0 : ntiles); tile += 2) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int cur = tile + u;
@@ -648,14 +769,16 @@ attn_kernel(AttnParams p) {
   using TT = AttnTile<DQK, DV, V_IN_K, MODE, C, WSPLIT, FP8>;
   __shared__ f32x4_t xch[WSPLIT > 1 ? 2 * TT::WG_WAVES * C * 64 : 1];
   __shared__ __attribute__((aligned(16))) uint8_t klds[TT::WG_WAVES * TT::KLDS_BYTES];
-  __shared__ int32_t qtok[MODE == kUnion ? 1 : TT::WG_WAVES * kQueueCap];
-  __shared__ uint32_t qbits[MODE == kUnion ? 1 : TT::WG_WAVES * kQueueCap];
+  constexpr int QCAP = MODE == kRowsMember ? kMemberQueueCap : kQueueCap;
+  __shared__ int32_t qtok[MODE == kUnion ? 1 : TT::WG_WAVES * QCAP];
+  __shared__ uint32_t qbits[MODE == kUnion ? 1 : TT::WG_WAVES * QCAP];
+  __shared__ uint32_t bmap[MODE == kRowsMember ? TT::WG_WAVES * 2 * kMemberWords : 1];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if constexpr (WSPLIT == 1)
-    attn_team<DQK, DV, V_IN_K, MODE, C, 1, FP8>(p, bid * 4 + w, 0, xch, klds, qtok, qbits);
+    attn_team<DQK, DV, V_IN_K, MODE, C, 1, FP8>(p, bid * 4 + w, 0, xch, klds, qtok, qbits, bmap);
   else
-    attn_team<DQK, DV, V_IN_K, MODE, C, WSPLIT, FP8>(p, bid, w, xch, klds, qtok, qbits);
+    attn_team<DQK, DV, V_IN_K, MODE, C, WSPLIT, FP8>(p, bid, w, xch, klds, qtok, qbits, bmap);
 }
 
 // Workgroups and threads per workgroup for a launch; false when one launch

@@ -45,6 +45,8 @@ hipError_t launch_attn_gqa256(AttnParams p, int union_mode, hipStream_t stream) 
   }
   const int r = p.group <= 8 ? 16 / p.group : 48 / p.group;
   p.rows_per_team = r < 4 ? r : 4;
+  // two-row one-wave teams (group 5-8) match their rows by membership
+  if (p.rows_per_team == 2 && p.group <= 8) return launch<kRowsMember, 1, 1>(p, stream);
   return launch_cols<kRows>(p, p.rows_per_team * p.group, stream);
 }
 
