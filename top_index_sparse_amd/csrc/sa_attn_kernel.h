@@ -408,6 +408,7 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   // their V is 0, multiplied by p = 0).
   const uint32_t k_row_bytes = (uint32_t)(2 * p.k_row_stride);   // < 2^32 (host check)
   const uint32_t v_row_bytes = (uint32_t)(2 * p.v_row_stride);
+  const bool v_like_k = v_row_bytes == k_row_bytes;
   // FP8 records: kvh's record of row 0 (k_row_stride counts 2-byte units)
   const uint8_t* kwb = FP8 ? reinterpret_cast<const uint8_t*>(p.k) + team_kv * k_row_bytes + kvh * 656
                            : reinterpret_cast<const uint8_t*>(kw);
@@ -471,11 +472,19 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
       }
       return;
     }
-    const int64_t voff = ok ? (int64_t)((uint64_t)(uint32_t)tl.tok * v_row_bytes) : -1;
     int klo[4], vlo[4], vhi[4];
     row_bcast4((int)koff, klo);
-    row_bcast4((int)voff, vlo);
-    row_bcast4((int)(voff >> 32), vhi);
+    if (v_like_k) {   // V rows at K's byte offsets (from their own base)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vlo[i] = klo[i];
+        vhi[i] = khi[i];
+      }
+    } else {
+      const int64_t voff = ok ? (int64_t)((uint64_t)(uint32_t)tl.tok * v_row_bytes) : -1;
+      row_bcast4((int)voff, vlo);
+      row_bcast4((int)(voff >> 32), vhi);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // K and V rows of slot 4g+i, bytes 256h + 16m: sixteen lanes per row
@@ -575,8 +584,7 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
 #pragma unroll
       for (int i = 0; i < 4; ++i) s2[i] = ((mask[c] >> i) & 1u) ? st[c][i] * sc : -INFINITY;
       float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = rows_max4(mx);
       const float m_cand = fmaxf(m_run[c], mx);
       const float m_new = m_cand > m_run[c] + kSlack ? m_cand : m_run[c];
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -728,8 +736,7 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ---------------------
 #pragma unroll
   for (int c = 0; c < C; ++c) {
-    float l = l_run[c] + __shfl_xor(l_run[c], 16);
-    l += __shfl_xor(l, 32);
+    const float l = rows_sum4(l_run[c]);
     bool live;
     int t, head;
     column(c, live, t, head);

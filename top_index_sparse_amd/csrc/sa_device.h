@@ -78,6 +78,36 @@ __device__ __forceinline__ int quad_bcast(int v) {
   return __builtin_amdgcn_mov_dpp(v, I * 0x55, 0xf, 0xf, false);
 }
 
+// Max and sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one per row of
+// 16), in every lane, with gfx950's row-swap permutes instead of an LDS
+// round trip. Both halves of a swap pair combine the same two operands in
+// the same order, so every lane gets the same bits.
+__device__ __forceinline__ void swap_pair(const u32x2_t r, float& a, float& b) {
+  const uint32_t x = r[0], y = r[1];   // (bit casts of vector elements read element 0)
+  a = __builtin_bit_cast(float, x);
+  b = __builtin_bit_cast(float, y);
+}
+
+__device__ __forceinline__ float rows_max4(float v) {
+  float a, b;
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  swap_pair(__builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane16_swap(u, u, false, false)), a, b);
+  v = fmaxf(a, b);
+  const uint32_t w = __builtin_bit_cast(uint32_t, v);
+  swap_pair(__builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane32_swap(w, w, false, false)), a, b);
+  return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float rows_sum4(float v) {
+  float a, b;
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  swap_pair(__builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane16_swap(u, u, false, false)), a, b);
+  v = a + b;
+  const uint32_t w = __builtin_bit_cast(uint32_t, v);
+  swap_pair(__builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane32_swap(w, w, false, false)), a, b);
+  return a + b;
+}
+
 // Lane L's value in every lane of its row of 16 (DPP row_newbcast:L).
 template <int L>
 __device__ __forceinline__ int row_bcast(int v) {
