@@ -511,6 +511,14 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
 
   int par = 0;
   uint8_t* lk = klds + wv * TT::KLDS_BYTES;   // this wave's K tile in LDS
+  // Byte position of 16-byte chunk c in a staged row. FP8 rows are written
+  // as dequantised pairs (lane n writes chunks 2n and 2n + 1), so their 32
+  // latent chunks are rotated within blocks of 8 (chunk c of block b sits at
+  // (c + b) mod 8): the pair writes, the V reads (chunk 16h + n of lane n)
+  // and the A-operand reads all stay free of bank conflicts.
+  auto cpos = [](int c) {
+    return 16 * (FP8 && c < 32 ? (c & ~7) | ((c + (c >> 3)) & 7) : c);
+  };
   auto compute = [&](const Data& td, const uint32_t mask[C]) {
     // Stage the gathered rows in LDS, in the A-operand order.
     if constexpr (FP8) {
@@ -532,9 +540,9 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
           b[2 * w] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
           b[2 * w + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
         }
-        uint8_t* row = lk + (4 * g + i) * KROW + 32 * n;
-        *reinterpret_cast<u32x4_t*>(row) = (u32x4_t){b[0], b[1], b[2], b[3]};
-        *reinterpret_cast<u32x4_t*>(row + 16) = (u32x4_t){b[4], b[5], b[6], b[7]};
+        uint8_t* row = lk + (4 * g + i) * KROW;
+        *reinterpret_cast<u32x4_t*>(row + cpos(2 * n)) = (u32x4_t){b[0], b[1], b[2], b[3]};
+        *reinterpret_cast<u32x4_t*>(row + cpos(2 * n + 1)) = (u32x4_t){b[4], b[5], b[6], b[7]};
       }
       *reinterpret_cast<u32x4_t*>(lk + (4 * g + (n >> 2)) * KROW + 16 * (MAIN / 8 + (n & 3))) = td.kd[4];
     } else if constexpr (VKLDS) {
@@ -560,7 +568,7 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     for (int c = 0; c < C; ++c) st[c] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lk + n * KROW + 64 * s + 16 * g);
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lk + n * KROW + cpos(4 * s + g));
 #pragma unroll
       for (int c = 0; c < C; ++c) st[c] = mfma_16x16x32(a, qop[c][s], st[c]);
     }
@@ -608,7 +616,7 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int h = 0; h < VCH; ++h)
-        vv[VCH * i + h] = VKLDS ? *reinterpret_cast<const u32x4_t*>(lk + (4 * g + i) * KROW + 256 * h + 16 * n)
+        vv[VCH * i + h] = VKLDS ? *reinterpret_cast<const u32x4_t*>(lk + (4 * g + i) * KROW + cpos(16 * h + n))
                                 : td.vd[VCH * i + h];
 #pragma unroll
     for (int mt = 0; mt < MTILES; ++mt) {
