@@ -324,3 +324,53 @@ def test_binding_rejects_undersized_outputs():
     with pytest.raises(ValueError):
         sa.sparse_attn_prefill_union(dev["q"], dev["k"], dev["v"], dev["idx"], 2, kv_len=501)
     assert sa.sa_call_count("sparse_attn_prefill") == before
+
+
+def _shuffled_ragged(seed, qlens, ctxs, topk, Hq=6):
+    """Ragged requests (group Hq over one KV head) with walk indices whose
+    slot order is shuffled in every row."""
+    rng = np.random.default_rng(seed)
+    cu_q = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    cu_kv = np.concatenate([[0], np.cumsum(ctxs)]).astype(np.int64)
+    T, KV = int(cu_q[-1]), int(cu_kv[-1])
+    q = gen.normal_bf16(rng, (T, Hq, 256))
+    k = gen.normal_bf16(rng, (KV, 1, 256))
+    v = gen.normal_bf16(rng, (KV, 1, 256))
+    idx = np.concatenate([gen.random_walk_indices(rng, np.arange(c - n, c), topk)
+                          for n, c in zip(qlens, ctxs) if n > 0]).astype(np.int32)
+    idx = gen.shuffle_slots(idx, seed + 1)
+    return gen.AttnCase("shuffled", q, k, v, idx, 1, 256, 256, 1 / 16, int(max(ctxs)),
+                        np.zeros(T, np.int64), cu_q, cu_kv)
+
+
+def test_membership_teams_edge_cases():
+    # Two-row teams (group 6) match their rows by membership: shuffled slot
+    # order, odd request lengths (teams straddling two requests), a request
+    # longer than the 32768-token bitmaps, a row holding a token twice and a
+    # row of padding fall back to matching by position.
+    say("[chunk] membership teams: shuffled rows, straddling teams, long request, duplicates")
+    qlens, ctxs = [7, 0, 12, 5, 9], [3000, 500, 33000, 900, 40000]
+    case = _shuffled_ragged(31, qlens, ctxs, 300)
+    idx = case.idx.copy()
+    idx[2, 10:20] = idx[2, 5]          # duplicates (row 2 and its team mate fall back)
+    idx[4, :] = -1                     # an empty row
+    idx[9, ::7] = 10 ** 6              # out-of-range slots
+    case.idx = idx
+    dev = attn_to_dev(case)
+    out, lse = _chunk(case, dev)
+    ro, rl = oracle.chunk_prefill(case.q, case.k, case.v, case.idx, case.cu_seqlens_q,
+                                  case.cu_seqlens_kv, num_kv_heads=1, scale=case.scale)
+    e, el = check_close(out, lse, ro, rl, "membership edge cases")
+    say(f"  max abs err O {e:.2e}  LSE {el:.2e}")
+
+
+@pytest.mark.parametrize("group", [5, 6, 7, 8])
+def test_membership_groups_and_topk_len(group):
+    say(f"[prefill] membership teams, group {group}, shuffled rows, per-row topk_len")
+    case = _small(40 + group, 33, 5000, 4900, group, 1, 700)
+    case.idx = gen.shuffle_slots(case.idx, 7)
+    tl = np.random.default_rng(group).integers(-3, 760, size=case.num_rows).astype(np.int32)
+    dev = attn_to_dev(case)
+    out, lse = _run_prefill(case, dev, topk_len=i32_dev(tl))
+    ro, rl = _oracle(case, topk_len=tl)
+    check_close(out, lse, ro, rl, f"membership group {group} with topk_len")
