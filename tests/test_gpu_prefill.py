@@ -102,6 +102,35 @@ def test_kv_len_smaller_than_buffer():
     check_close(out, lse, ro, rl, "kv_len")
 
 
+@pytest.mark.parametrize("mla", [False, True])
+def test_row_stride_past_descriptor_field(mla):
+    # K rows 16,400 bytes apart (past the 14-bit stride of a buffer
+    # descriptor): the gathers take 64-bit addresses; same results
+    say(f"[prefill] K row stride 8200 elements, {'MLA' if mla else 'GQA'}")
+    if mla:
+        case = gen.make_attn_case("small", seed=19, num_rows=21, kv_len=700, first_pos=680,
+                                  num_q_heads=8, num_kv_heads=1, head_dim_qk=576,
+                                  head_dim_v=512, topk=300, v_in_k=True, walk=True)
+    else:
+        case = _small(19, 21, 700, 680, 12, 1, 300)
+    dqk = case.head_dim_qk
+    dev = attn_to_dev(case)
+    kp = torch.zeros((case.kv_len, 8200), dtype=torch.bfloat16, device="cuda")
+    kp[:, :dqk] = dev["k"].reshape(case.kv_len, dqk)
+    kw = kp[:, :dqk].view(case.kv_len, 1, dqk)
+    if mla:
+        out, lse = sa.sparse_attn_prefill(dev["q"], kw, None, dev["idx"], sm_scale=case.scale,
+                                          head_dim_v=case.head_dim_v)
+    else:
+        vp = torch.zeros((case.kv_len, 8200), dtype=torch.bfloat16, device="cuda")
+        vp[:, :256] = dev["v"].reshape(case.kv_len, 256)
+        out, lse = sa.sparse_attn_prefill(dev["q"], kw, vp[:, :256].view(case.kv_len, 1, 256),
+                                          dev["idx"], sm_scale=case.scale)
+    torch.cuda.synchronize()
+    ro, rl = _oracle(case)
+    check_close(out, lse, ro, rl, "wide stride")
+
+
 def test_strided_rows_and_full_overwrite():
     say("[prefill] padded row strides, NaN-poisoned outputs, guard bands")
     case = _small(15, 13, 800, 780, 12, 1, 200)

@@ -132,15 +132,18 @@ struct AttnTile {
   };
 };
 
-// What an invalid slot's lanes load instead of a K or V row: zeros, so the
-// loads need no branch (a load under a per-lane branch cannot be counted,
-// and waiting for any later load then waits for all of them) and an invalid
-// slot's V is exactly 0. Every row offset read here is below 2 KB.
+// Invalid slots load zeros, so the loads need no branch (a load under a
+// per-lane branch cannot be counted, and waiting for any later load then
+// waits for all of them) and an invalid slot's V is exactly 0. Row gathers
+// through buffer descriptors (BUF) name the absent row kNoRow; 64-bit
+// addressed gathers (windows past 2 GiB, strides past the descriptor's
+// field, paged records) read this zero row instead. Every row offset read
+// here is below 2 KB.
 static __device__ __attribute__((aligned(16))) uint8_t kZeroRow[2048];
 
 // Team `team_id`, wavefront `split` of WSPLIT. xch: partial-score exchange
 // [2][WG_WAVES][C][64]; klds: per-wave K tiles; qtok/qbits: per-wave queues.
-template <int DQK, int DV, bool V_IN_K, int MODE, int C, int WSPLIT, bool FP8>
+template <int DQK, int DV, bool V_IN_K, int MODE, int C, int WSPLIT, bool FP8, bool BUF>
 __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int split,
                                           f32x4_t* xch, uint8_t* klds, int32_t* qtok_all,
                                           uint32_t* qbits_all, uint32_t* bmap_all) {
@@ -159,11 +162,12 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   constexpr int CPR = TT::CPR;
   constexpr int TILE = 16;
   using Data = typename TT::Data;
+  static_assert(!(BUF && DECODE), "paged records are gathered with 64-bit addresses");
 
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int n = lane & 15;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int group = p.group;
   const int slot_l = 4 * g + (n >> 2);   // index lanes: slot and row read by this lane
   const int row_l = n & 3;
@@ -352,18 +356,22 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   }
 
   // One index load per lane per tile (plus the ownership byte in union mode).
+  // Lanes past their row's end read entry 0 (every row that has a tile has
+  // one) and the entry is discarded where it is used: the load carries no
+  // branch and nothing reads it early, so waiting for this tile's indices
+  // does not wait for the next tile's, issued after them.
+  const int jlim = UNION ? jmax : jmax_l;   // this lane's entries
   struct Idx {
     int x;        // per-token: index of (row_l, slot_l); union: list entry slot_l
+    int j;        // its position (the entry exists iff j < jlim)
     uint32_t b;   // union: its ownership bits
   };
   auto load_idx = [&](Idx& ti, int j0) {
     const int jk = j0 + slot_l;
-    if (UNION) {
-      ti.x = jk < jmax ? irow[jk] : -1;
-      ti.b = jk < jmax ? (uint32_t)brow[jk] : 0u;
-    } else {
-      ti.x = jk < jmax_l ? irow[jk] : -1;
-    }
+    const int jr = jk < jlim ? jk : 0;
+    ti.x = irow[jr];
+    ti.j = jk;
+    if (UNION) ti.b = brow[jr];
   };
 
   // The queue of tokens still to gather (per wave, in LDS).
@@ -382,7 +390,7 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   // row 0's; every other token is queued once per run of consecutive rows
   // that hold it.
   auto resolve = [&](const Idx& ti) -> Tile {
-    const int gt = (unsigned)ti.x < (unsigned)len_l ? base_l + ti.x : -1;
+    const int gt = ti.j < jlim && (unsigned)ti.x < (unsigned)len_l ? base_l + ti.x : -1;
     const int m0 = quad_bcast<0>(gt);                                            // row 0
     const int pv = __builtin_amdgcn_mov_dpp(gt, 0x90, 0xf, 0xf, false);          // row r-1: [0,0,1,2]
     const bool eqm = gt >= 0 && gt == m0;
@@ -414,10 +422,57 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
                            : reinterpret_cast<const uint8_t*>(kw);
   const uint8_t* kbn = kwb + 16 * n;   // this lane's 16 bytes of a 256-byte half row
   const uint8_t* vbn = reinterpret_cast<const uint8_t*>(vw) + 16 * n;
+  // BUF: K and V rows as windows of row-strided records from the same bases
+  // (the launcher checks that strides and windows fit the descriptors).
+  const rows_rsrc_t rk = rows_rsrc(kwb, k_row_bytes);
+  const rows_rsrc_t rv = rows_rsrc(vw, v_row_bytes);
   // Issues a tile's loads; returns the score masks: bit i of mask[c] set
   // when slot 4g+i contributes to column n of tile c.
   auto load_data = [&](Data& td, const Tile& tl, uint32_t mask[C]) {
     const bool ok = tl.tok >= 0 && (tl.bits & team_bits);
+    if constexpr (BUF) {
+      // The index lane's row (kNoRow when invalid) and bits reach the
+      // sixteen lanes of group g by row broadcast; an invalid slot owns no
+      // column.
+      int rw[4], bq[4];
+      row_bcast4(ok ? tl.tok : kNoRow, rw);
+      row_bcast4(ok ? (int)tl.bits : 0, bq);
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        uint32_t mk = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mk |= (uint32_t)(((uint32_t)bq[i] & col_bit[c]) != 0u) << i;
+        mask[c] = mk;
+      }
+      if constexpr (FP8) {
+        // as below: latent half rows, one rope chunk, the slot's scales
+        const int ir = n >> 2, is = n & 3;
+        auto pick = [](const int a[4], int i) { return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3]; };
+#pragma unroll
+        for (int i = 0; i < 4; ++i) td.kd[i] = ld_row16(rk, rw[i], 256 * split + 16 * n);
+        td.kd[4] = ld_row16(rk, pick(rw, ir), 528 + 64 * split + 16 * is);
+        td.kd[5] = ld_row16(rk, pick(rw, is), 512);
+      } else if constexpr (VKLDS) {
+#pragma unroll
+        for (int q = 0; q < KSTEPS; ++q) {
+          const int i0 = (16 * q) / CPR;
+          const int c = 16 * q + n;
+          const bool nx = i0 < 3 && c >= CPR * (i0 + 1);
+          const int ch = c - CPR * (nx ? i0 + 1 : i0);
+          const int d = ch < MAIN / 8 ? split * MAIN + 8 * ch : DV + split * ROPE + 8 * (ch - MAIN / 8);
+          td.kd[q] = ld_row16(rk, nx ? rw[i0 < 3 ? i0 + 1 : 3] : rw[i0], 2 * d);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int h = 0; h < KCH; ++h) td.kd[KCH * i + h] = ld_row16(rk, rw[i], 16 * n + 256 * h);
+#pragma unroll
+          for (int h = 0; h < VCH; ++h) td.vd[VCH * i + h] = ld_row16(rv, rw[i], 16 * n + 256 * h);
+        }
+      }
+      return;
+    }
     int64_t koff;
     if constexpr (DECODE)   // record (t & mask) of page t >> shift (page stride < 2^32)
       koff = ok ? (int64_t)((uint64_t)((uint32_t)tl.tok >> p.page_shift) * (uint32_t)p.page_stride +
@@ -588,25 +643,28 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     i16x4_t pop[C];
 #pragma unroll
     for (int c = 0; c < C; ++c) {
+      // Masked raw scores; scaling commutes with the max (sc > 0 and
+      // rounding is monotonic), and each probability takes one fma.
       float s2[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s2[i] = ((mask[c] >> i) & 1u) ? st[c][i] * sc : -INFINITY;
+      for (int i = 0; i < 4; ++i) s2[i] = ((mask[c] >> i) & 1u) ? st[c][i] : -INFINITY;
       float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
-      mx = rows_max4(mx);
-      const float m_cand = fmaxf(m_run[c], mx);
+      mx = rows_max4(mx) * sc;
+      const float m_cand = max2(m_run[c], mx);
       const float m_new = m_cand > m_run[c] + kSlack ? m_cand : m_run[c];
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[c] - m_use);
       float pr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s2[i] - m_use);
-      l_run[c] = l_run[c] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(s2[i], sc, -m_use));
       // Rescale only when some column's reference max moved (alpha == 1
       // elsewhere).
       if (__builtin_amdgcn_ballot_w64(m_new != m_run[c])) {
+        const float alpha = fast_exp2(m_run[c] - m_use);
+        l_run[c] *= alpha;
 #pragma unroll
         for (int mt = 0; mt < MTILES; ++mt) acc[c][mt] *= alpha;
       }
+      l_run[c] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
       m_run[c] = m_new;
       pop[c] = __builtin_bit_cast(i16x4_t,
                                   (u32x2_t){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
@@ -714,12 +772,14 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     for (int u = 0; u < 2; ++u) {
       const int cur = tile + u;
       if (cur >= ntiles) break;
-      if (cur + 1 < ntiles) load_idx(ib[u ^ 1], (tile_first + (cur + 1) * tile_step) * TILE);
+      // (after the last tile this reads entry 0 and is never used)
+      load_idx(ib[u ^ 1], (tile_first + (cur + 1) * tile_step) * TILE);
       __builtin_amdgcn_sched_barrier(0);
       Tile tl;
       if constexpr (UNION) {
-        tl.tok = (unsigned)ib[u].x < (unsigned)len_l ? ib[u].x : -1;
-        tl.bits = ib[u].b;
+        const bool in = ib[u].j < jlim;
+        tl.tok = in && (unsigned)ib[u].x < (unsigned)len_l ? ib[u].x : -1;
+        tl.bits = in ? ib[u].b : 0u;
       } else {
         tl = resolve(ib[u]);
       }
@@ -775,6 +835,17 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   }
 }
 
+// Whether every K and V row a launch can name is reachable through a row
+// buffer descriptor from the teams' bases: both strides fit the descriptor's
+// field and the launch's KV rows span at most 2 GiB at the larger stride.
+__device__ __forceinline__ bool rows_fit_rsrc(const AttnParams& p) {
+  const uint64_t kb = 2 * (uint64_t)p.k_row_stride, vb = 2 * (uint64_t)p.v_row_stride;
+  const int64_t rows = p.cu_kv ? p.cu_kv[p.num_reqs] : (int64_t)p.kv_len;
+  const uint64_t stride = kb > vb ? kb : vb;
+  return kb <= kMaxRowStride && vb <= kMaxRowStride && rows >= 0 &&
+         (uint64_t)rows * stride <= (1ull << 31);
+}
+
 // WSPLIT = 1: four independent one-wave teams per workgroup. WSPLIT = 2:
 // one team per workgroup, its two halves exchanging partial scores.
 template <int DQK, int DV, bool V_IN_K, int MODE, int C, int WSPLIT, bool FP8, int WAVES>
@@ -790,10 +861,14 @@ attn_kernel(AttnParams p) {
   __shared__ uint32_t bmap[MODE == kRowsMember ? TT::WG_WAVES * 2 * kMemberWords : 1];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if constexpr (WSPLIT == 1)
-    attn_team<DQK, DV, V_IN_K, MODE, C, 1, FP8>(p, bid * 4 + w, 0, xch, klds, qtok, qbits, bmap);
+  const int team = WSPLIT == 1 ? bid * 4 + w : bid;
+  const int split = WSPLIT == 1 ? 0 : w;
+  if constexpr (MODE == kDecode)
+    attn_team<DQK, DV, V_IN_K, MODE, C, WSPLIT, FP8, false>(p, team, split, xch, klds, qtok, qbits, bmap);
+  else if (rows_fit_rsrc(p))
+    attn_team<DQK, DV, V_IN_K, MODE, C, WSPLIT, FP8, true>(p, team, split, xch, klds, qtok, qbits, bmap);
   else
-    attn_team<DQK, DV, V_IN_K, MODE, C, WSPLIT, FP8>(p, bid, w, xch, klds, qtok, qbits, bmap);
+    attn_team<DQK, DV, V_IN_K, MODE, C, WSPLIT, FP8, false>(p, team, split, xch, klds, qtok, qbits, bmap);
 }
 
 // Workgroups and threads per workgroup for a launch; false when one launch

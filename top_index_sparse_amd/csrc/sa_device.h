@@ -48,6 +48,37 @@ __device__ __forceinline__ void st16(void* p, f32x4_t v) {
   *reinterpret_cast<f32x4_t*>(p) = v;
 }
 
+// Row gathers through a structured buffer descriptor (MUBUF idxen + offen):
+// 16 bytes at base + row * stride + off. Measured on gfx950: the byte offset
+// row * stride + off is a 32-bit quantity (it wraps past 4 GiB), the stride
+// field holds 14 bits, and a row >= num_records reads zeros without touching
+// memory, which is how invalid slots are served. Windows are kept within
+// 2 GiB of base, where no reading of the offset's top bit matters.
+typedef __amdgpu_buffer_rsrc_t rows_rsrc_t;
+__device__ u32x4_t sa_struct_buffer_load_v4(rows_rsrc_t r, int row, int off, int soff, int aux)
+    __asm("llvm.amdgcn.struct.ptr.buffer.load.v4i32");
+
+constexpr int kNoRow = 0x7fffffff;         // a row index every window treats as absent
+constexpr uint32_t kMaxRowStride = 16383;  // bytes (14-bit field)
+
+__device__ __forceinline__ rows_rsrc_t rows_rsrc(const void* base, uint32_t stride) {
+  // num_records = kNoRow: rows are bounded by the kernel's own checks; 0x20000
+  // is gfx9's untyped 32-bit data format word.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)stride, kNoRow,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4_t ld_row16(rows_rsrc_t r, int row, int off) {
+  return sa_struct_buffer_load_v4(r, row, off, 0, 0);
+}
+
+// Lane L's value of each row of 16 added to y in one DPP operation
+// (row_newbcast:L on the add's first operand).
+template <int L>
+__device__ __forceinline__ int row_bcast_add(int v, int y) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x150 + L, 0xf, 0xf, true) + y;
+}
+
 // Two fp32 values to packed bf16 (round to nearest even), low half first.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2_t h = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
@@ -88,14 +119,23 @@ __device__ __forceinline__ void swap_pair(const u32x2_t r, float& a, float& b) {
   b = __builtin_bit_cast(float, y);
 }
 
+// max(a, b) as one v_max_f32: fmaxf first quiets each operand that the
+// compiler cannot prove canonical (a cross-lane result, a loop-carried
+// value), one extra instruction per operand. Scores here are never NaN.
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ float rows_max4(float v) {
   float a, b;
   const uint32_t u = __builtin_bit_cast(uint32_t, v);
   swap_pair(__builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane16_swap(u, u, false, false)), a, b);
-  v = fmaxf(a, b);
+  v = max2(a, b);
   const uint32_t w = __builtin_bit_cast(uint32_t, v);
   swap_pair(__builtin_bit_cast(u32x2_t, __builtin_amdgcn_permlane32_swap(w, w, false, false)), a, b);
-  return fmaxf(a, b);
+  return max2(a, b);
 }
 
 __device__ __forceinline__ float rows_sum4(float v) {
