@@ -102,7 +102,7 @@ def load_counters():
 
 
 def team_tiles(idx: np.ndarray, kv_len, rows_per_team: int, cu_q=None, cu_kv=None,
-               every_tile: bool = False):
+               every_tile: bool = False, member: bool = False):
     """Slot tiles the per-token team kernel issues, from the index rows.
 
     A team takes `rows_per_team` consecutive rows and walks their slots in
@@ -112,6 +112,9 @@ def team_tiles(idx: np.ndarray, kv_len, rows_per_team: int, cu_q=None, cu_kv=Non
     the queue is gathered 16 tokens at a time. A tile with no valid token of
     the first row is skipped (`every_tile`: the three-tile shape issues all).
     Tokens are compared as global KV rows (request base + local index).
+    `member` (two-row membership teams): a team whose two rows share one
+    request of at most 32768 tokens and hold no token twice streams the
+    union of its rows' sets instead, ceil(|union| / 16) tiles.
 
     Returns (tiles issued per KV head, valid K/V rows gathered per KV head).
     """
@@ -135,7 +138,8 @@ def team_tiles(idx: np.ndarray, kv_len, rows_per_team: int, cu_q=None, cu_kv=Non
     X = X.reshape(teams, R, nt * 16)
     row0 = X[:, 0, :]
     first = row0 >= 0
-    primary = teams * nt if every_tile else int(first.reshape(teams, nt, 16).any(-1).sum())
+    primary = (np.full(teams, nt) if every_tile
+               else first.reshape(teams, nt, 16).any(-1).sum(-1))
     queued = np.zeros(teams, dtype=np.int64)
     for r in range(1, R):
         x = X[:, r, :]
@@ -143,8 +147,25 @@ def team_tiles(idx: np.ndarray, kv_len, rows_per_team: int, cu_q=None, cu_kv=Non
         if r >= 2:
             start &= x != X[:, r - 1, :]
         queued += start.sum(-1)
-    tiles = primary + int(((queued + 15) // 16).sum())
-    return tiles, int(first.sum() + queued.sum())
+    tiles_t = primary + (queued + 15) // 16
+    rows_t = first.sum(-1) + queued
+    if member and R == 2:
+        rows2 = np.arange(teams) * 2 + 1 < T
+        if cu_q is None:
+            same = np.full(teams, kv_len <= 32768)
+        else:
+            r2 = req.reshape(teams, 2)
+            ln = np.asarray(length).reshape(teams, 2)
+            same = (r2[:, 0] == r2[:, 1]) & (ln[:, 0] <= 32768)
+        srt = np.sort(X, axis=-1)
+        dup = ((srt[..., 1:] == srt[..., :-1]) & (srt[..., 1:] >= 0)).any(-1).any(-1)
+        both = np.sort(X.reshape(teams, -1), axis=-1)
+        inter = ((both[:, 1:] == both[:, :-1]) & (both[:, 1:] >= 0)).sum(-1)
+        union = (both >= 0).sum(-1) - inter
+        qual = rows2 & same & ~dup
+        tiles_t = np.where(qual, (union + 15) // 16, tiles_t)
+        rows_t = np.where(qual, union, rows_t)
+    return int(tiles_t.sum()), int(rows_t.sum())
 
 
 # ----------------------------------------------------------- CPU baseline
@@ -302,7 +323,7 @@ def measure_others(args, sa, torch, stream):
     ms = _events_ms(torch, stream, lambda: sa.sparse_attn_chunk_prefill(
         q, k, v, sidx, cu_q1, cu_kv1, sm_scale=c.scale, out=out, lse=lse, stream=stream), w, n)
     r = _l1(_rate(per_token_bytes, ms),
-            team_tiles(gen.shuffle_slots(c.idx, args.seed + 1), c.kv_len, 2)[0] * 16 * 1024)
+            team_tiles(gen.shuffle_slots(c.idx, args.seed + 1), c.kv_len, 2, member=True)[0] * 16 * 1024)
     ms_u = _events_ms(torch, stream, lambda: sa.sparse_attn_prefill_union(
         q, k, v, sidx, 2, sm_scale=c.scale, ws=ws, out=out, lse=lse, stream=stream), w, n)
     r.update({"union_G2_ms": round(ms_u, 4)})
@@ -421,7 +442,7 @@ def measure_others(args, sa, torch, stream):
         q, k, v, idx, cu_q, cu_kv, sm_scale=c.scale, out=out, lse=lse, stream=stream), w, n)
     res["ragged_chunk_prefill"] = _l1(
         _rate(gathered_bytes(c), ms),
-        team_tiles(c.idx, None, 2, c.cu_seqlens_q, c.cu_seqlens_kv)[0] * 16 * 1024)
+        team_tiles(c.idx, None, 2, c.cu_seqlens_q, c.cu_seqlens_kv, member=True)[0] * 16 * 1024)
     res["ragged_chunk_prefill"]["rows"] = c.num_rows
     # union mode over the same ragged requests (groups of 2 rows per request)
     ws = torch.empty(sa.sparse_attn_chunk_union_workspace_bytes(c.num_rows, len(cu_q) - 1,
@@ -634,7 +655,7 @@ def main():
     # The vector L1 bytes the kernel's loads request: every slot tile a team
     # issues loads 16 K rows and 16 V rows (512 B each; invalid slots read a
     # cached row of zeros). Two rows x 6 heads share one 16-column tile.
-    tiles, rows_gathered = team_tiles(case.idx, case.kv_len, 2)
+    tiles, rows_gathered = team_tiles(case.idx, case.kv_len, 2, member=True)
     l1_bytes = tiles * 16 * 1024 * case.num_kv_heads
     l1_gbs = l1_bytes / (kernel_ms * 1e-3) / 1e9
     # Issued MFMA work per tile: S^T over 8 k-steps of 16x16x32 and O^T over
