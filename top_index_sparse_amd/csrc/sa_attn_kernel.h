@@ -333,7 +333,7 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     t = t0 + (live ? j : 0);
     return live ? (1u << (bit0 + j)) : 0u;
   };
-  uint32_t col_bit[C];
+  int col_sh[C];   // the column's ownership bit (31 for a dead column: no bit is that high)
   // Wave-uniform K/V bases; lane offsets are added per load.
   const uint16_t* kw = p.k + team_kv * p.k_row_stride + kvh * DQK + (VKLDS ? 0 : 32 * KSTEPS * split);
   const uint16_t* vw = p.v + team_kv * p.v_row_stride + kvh * (V_IN_K ? DQK : DV) + 128 * VCH * split;
@@ -344,7 +344,8 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   for (int c = 0; c < C; ++c) {
     bool live;
     int t, head;
-    col_bit[c] = column(c, live, t, head);
+    const uint32_t cb = column(c, live, t, head);
+    col_sh[c] = live ? __builtin_ctz(cb) : 31;
     const uint16_t* qp = p.q + (int64_t)(t / qrow_div) * p.q_row_stride + (int64_t)head * DQK + 8 * g;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
@@ -426,24 +427,18 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   // (the launcher checks that strides and windows fit the descriptors).
   const rows_rsrc_t rk = rows_rsrc(kwb, k_row_bytes);
   const rows_rsrc_t rv = rows_rsrc(vw, v_row_bytes);
-  // Issues a tile's loads; returns the score masks: bit i of mask[c] set
-  // when slot 4g+i contributes to column n of tile c.
-  auto load_data = [&](Data& td, const Tile& tl, uint32_t mask[C]) {
+  // Issues a tile's loads; returns the ownership bits of slots 4g..4g+3
+  // (0 for an invalid slot): slot 4g+i contributes to column n of tile c iff
+  // bit col_sh[c] of own[i] is set.
+  auto load_data = [&](Data& td, const Tile& tl, int own[4]) {
     const bool ok = tl.tok >= 0 && (tl.bits & team_bits);
     if constexpr (BUF) {
       // The index lane's row (kNoRow when invalid) and bits reach the
       // sixteen lanes of group g by row broadcast; an invalid slot owns no
       // column.
-      int rw[4], bq[4];
+      int rw[4];
       row_bcast4(ok ? tl.tok : kNoRow, rw);
-      row_bcast4(ok ? (int)tl.bits : 0, bq);
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        uint32_t mk = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mk |= (uint32_t)(((uint32_t)bq[i] & col_bit[c]) != 0u) << i;
-        mask[c] = mk;
-      }
+      row_bcast4(ok ? (int)tl.bits : 0, own);
       if constexpr (FP8) {
         // as below: latent half rows, one rope chunk, the slot's scales
         const int ir = n >> 2, is = n & 3;
@@ -480,16 +475,9 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
                 : -1;
     else
       koff = ok ? (int64_t)((uint64_t)(uint32_t)tl.tok * k_row_bytes) : -1;
-    int khi[4], bq[4];
+    int khi[4];
     row_bcast4((int)(koff >> 32), khi);
-    row_bcast4((int)tl.bits, bq);
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      uint32_t mk = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mk |= (uint32_t)(khi[i] >= 0 && ((uint32_t)bq[i] & col_bit[c])) << i;
-      mask[c] = mk;
-    }
+    row_bcast4(ok ? (int)tl.bits : 0, own);
     if constexpr (FP8) {
       // Per slot 4g+i: the wave's 256 latent bytes, sixteen lanes per row.
       // Per lane: one rope chunk (slot 4g + n/4, chunk n%4 of the wave's 64
@@ -553,11 +541,16 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     }
   };
 
-  float m_run[C], l_run[C];   // reference max (log2 domain) and this lane's share of the sum
+  // Reference max (log2 domain) and this lane's share of the sum. The max
+  // starts at -FLT_MAX, not -inf: it stays finite, so a column that has seen
+  // no valid score yet needs no special case (its masked scores give
+  // exp2(-inf) = 0, and the first valid score moves the max and scales the
+  // empty state by exp2(-FLT_MAX - m) = 0).
+  float m_run[C], l_run[C];
   f32x4_t acc[C][MTILES];
 #pragma unroll
   for (int c = 0; c < C; ++c) {
-    m_run[c] = -INFINITY;
+    m_run[c] = -__FLT_MAX__;
     l_run[c] = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MTILES; ++mt) acc[c][mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -574,7 +567,7 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   auto cpos = [](int c) {
     return 16 * (FP8 && c < 32 ? (c & ~7) | ((c + (c >> 3)) & 7) : c);
   };
-  auto compute = [&](const Data& td, const uint32_t mask[C]) {
+  auto compute = [&](const Data& td, const int own[4]) {
     // Stage the gathered rows in LDS, in the A-operand order.
     if constexpr (FP8) {
       // Dequantise: latent chunk n of slot 4g+i (values 16n .. 16n+15 of the
@@ -647,19 +640,17 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
       // rounding is monotonic), and each probability takes one fma.
       float s2[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s2[i] = ((mask[c] >> i) & 1u) ? st[c][i] : -INFINITY;
-      float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
+      for (int i = 0; i < 4; ++i) s2[i] = keep_if_bit(st[c][i], own[i], col_sh[c]);
+      float mx = max4(s2[0], s2[1], s2[2], s2[3]);
       mx = rows_max4(mx) * sc;
-      const float m_cand = max2(m_run[c], mx);
-      const float m_new = m_cand > m_run[c] + kSlack ? m_cand : m_run[c];
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float m_new = mx > m_run[c] + kSlack ? mx : m_run[c];
       float pr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(s2[i], sc, -m_use));
+      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(s2[i], sc, -m_new));
       // Rescale only when some column's reference max moved (alpha == 1
       // elsewhere).
       if (__builtin_amdgcn_ballot_w64(m_new != m_run[c])) {
-        const float alpha = fast_exp2(m_run[c] - m_use);
+        const float alpha = fast_exp2(m_run[c] - m_new);
         l_run[c] *= alpha;
 #pragma unroll
         for (int mt = 0; mt < MTILES; ++mt) acc[c][mt] *= alpha;
@@ -692,9 +683,9 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     while (qcount >= 16 || (flush && qcount > 0)) {
       const bool have = slot_l < qcount;
       const Tile tl{have ? qtok[slot_l] : -1, have ? qbits[slot_l] : 0u};
-      uint32_t mask[C];
-      load_data(db, tl, mask);
-      compute(db, mask);
+      int own[4];
+      load_data(db, tl, own);
+      compute(db, own);
       // move the remaining entries down (in-order LDS: reads first)
       const int rem = qcount > 16 ? qcount - 16 : 0;
       const bool mv = lane < rem;
@@ -746,9 +737,9 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
       while (qcount - head >= 16 || (last && qcount - head > 0)) {
         const bool have = slot_l < qcount - head;
         const Tile tl{have ? qtok[head + slot_l] : -1, have ? qbits[head + slot_l] : 0u};
-        uint32_t mask[C];
-        load_data(db, tl, mask);
-        compute(db, mask);
+        int own[4];
+        load_data(db, tl, own);
+        compute(db, own);
         head += 16;
       }
       const int rem = qcount > head ? qcount - head : 0;
@@ -789,10 +780,10 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
       // (The three-tile shape keeps the straight path: the branch costs it
       // more register spills than the tiles it could skip.)
       if (C == 3 || __ballot(tl.tok >= 0 && (tl.bits & team_bits)) != 0) {
-        uint32_t mask[C];
-        load_data(db, tl, mask);
+        int own[4];
+        load_data(db, tl, own);
         __builtin_amdgcn_sched_barrier(0);
-        compute(db, mask);
+        compute(db, own);
       }
       // per-token modes: queue tiles whenever 16 queued tokens wait (so the
       // queue never holds more than 63), and a last one for the rest

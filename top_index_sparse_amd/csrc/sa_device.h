@@ -72,6 +72,13 @@ __device__ __forceinline__ u32x4_t ld_row16(rows_rsrc_t r, int row, int off) {
   return sa_struct_buffer_load_v4(r, row, off, 0, 0);
 }
 
+// x where bit `pos` of `bits` is set, else -inf: the sign-extended one-bit
+// field selects between the two bit patterns (v_bfe_i32, v_bitop3_b32).
+__device__ __forceinline__ float keep_if_bit(float x, int bits, int pos) {
+  const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe(bits, pos, 1);
+  return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, x) & m) | (0xff800000u & ~m));
+}
+
 // Lane L's value of each row of 16 added to y in one DPP operation
 // (row_newbcast:L on the add's first operand).
 template <int L>
@@ -126,6 +133,12 @@ __device__ __forceinline__ float max2(float a, float b) {
   float r;
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
+}
+
+__device__ __forceinline__ float max4(float a, float b, float c, float d) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return max2(r, d);
 }
 
 __device__ __forceinline__ float rows_max4(float v) {
