@@ -383,7 +383,13 @@ def measure_others(args, sa, torch, stream):
     ms = _events_ms(torch, stream, lambda: sa.sparse_attn_prefill(
         q, k, None, idx, sm_scale=c.scale, head_dim_v=512, out=out, lse=lse, stream=stream), w, n)
     res["mla_per_token"] = _l1(_rate(per_token_bytes, ms),
-                               team_tiles(c.idx, c.kv_len, 2)[0] * 16 * 1152)
+                               team_tiles(c.idx, c.kv_len, 2, member=True)[0] * 16 * 1152)
+    # the same sets with every row's slots shuffled (membership teams)
+    sidx = torch.from_numpy(gen.shuffle_slots(c.idx, args.seed + 1)).cuda()
+    ms = _events_ms(torch, stream, lambda: sa.sparse_attn_prefill(
+        q, k, None, sidx, sm_scale=c.scale, head_dim_v=512, out=out, lse=lse, stream=stream), w, n)
+    res["mla_per_token_shuffled_slots"] = _rate(per_token_bytes, ms)
+    del sidx
     for G in (2, 4):
         ws = torch.empty(sa.sparse_attn_union_workspace_bytes(c.num_rows, c.topk, G),
                          dtype=torch.uint8, device="cuda")

@@ -102,3 +102,38 @@ def test_fp8_ragged_chunk_prefill():
     torch.cuda.synchronize()
     assert st == sa.SA_OK
     check_close(uo, ul, ro, rl, "fp8 ragged union")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_mla_membership_teams_edge_cases(fp8):
+    # Two-row MLA teams (8 heads) match their rows by membership through a
+    # bitmap pair the team's two waves share: shuffled slot order, odd request
+    # lengths (teams straddling two requests), a request longer than the
+    # 32768-token bitmaps, a row holding a token twice and a row of padding
+    # fall back to matching by position.
+    say(f"[chunk] MLA membership teams ({'FP8 records' if fp8 else 'bf16 rows'}): shuffled, "
+        "straddling, long request, duplicates")
+    rng = np.random.default_rng(91 + fp8)
+    qlens, ctxs, topk = [7, 0, 12, 5, 9], [3000, 500, 33000, 900, 40000], 300
+    cu_q = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    cu_kv = np.concatenate([[0], np.cumsum(ctxs)]).astype(np.int64)
+    T, KV = int(cu_q[-1]), int(cu_kv[-1])
+    q = gen.normal_bf16(rng, (T, 8, 576))
+    k = (gen.mla_fp8_rows(rng, KV).reshape(KV, 1, gen.FP8_ROW_BYTES) if fp8
+         else gen.normal_bf16(rng, (KV, 1, 576)))
+    idx = np.concatenate([gen.random_walk_indices(rng, np.arange(c - n, c), topk)
+                          for n, c in zip(qlens, ctxs) if n > 0]).astype(np.int32)
+    idx = gen.shuffle_slots(idx, 5)
+    idx[2, 10:20] = idx[2, 5]          # duplicates (row 2 and its team mate fall back)
+    idx[4, :] = -1                     # an empty row
+    idx[9, ::7] = 10 ** 6              # out-of-range slots
+    scale = 1 / 24
+    kd = oracle.mla_fp8_rows_to_f64(k) if fp8 else k
+    out, lse = sa.sparse_attn_chunk_prefill(bf16_dev(q), _u8_dev(k) if fp8 else bf16_dev(k), None,
+                                            i32_dev(idx), i32_dev(cu_q), i64_dev(cu_kv),
+                                            sm_scale=scale, head_dim_v=512)
+    torch.cuda.synchronize()
+    ro, rl = oracle.chunk_prefill(q, kd, None, idx, cu_q, cu_kv, num_kv_heads=1, scale=scale,
+                                  head_dim_v=512)
+    e, el = check_close(out, lse, ro, rl, "MLA membership edge cases")
+    say(f"  max abs err O {e:.2e}  LSE {el:.2e}")

@@ -73,16 +73,17 @@ namespace sa {
 
 // kRows: per-token results (one request, or ragged requests when cu_q is
 // set), rows grouped into teams by position. kRowsMember: the same for
-// two-row one-wave teams, which match their rows' tokens by membership
-// (LDS bitmaps of each row's set) instead of by slot position wherever the
-// team qualifies (see below), and by position elsewhere. kUnion: prebuilt
+// two-row teams (one wave, or two waves sharing the team's bitmaps), which
+// match their rows' tokens by membership (LDS bitmaps of each row's set)
+// instead of by slot position wherever the team qualifies (see below), and
+// by position elsewhere. kUnion: prebuilt
 // union lists. kDecode: one team per (request, slot range) over paged FP8
 // records, each writing that range's normalised result for a later merge;
 // range s of S takes the request's slot tiles s, s + S, s + 2S, ...
 enum : int { kRows = 0, kUnion = 1, kDecode = 2, kRowsMember = 3 };
 
 // Membership bitmaps: one bit per token of the team's request, one bitmap
-// per row, per wavefront; requests longer than this match by position.
+// per row, per team; requests longer than this match by position.
 constexpr int kMemberTokens = 32768;
 constexpr int kMemberWords = kMemberTokens / 32;
 
@@ -119,7 +120,9 @@ struct AttnTile {
   // block scales, 64 bf16 rope values), dequantised into the same bf16 slice
   static_assert(!FP8 || (VKLDS && DQK == 576 && DV == 512 && WSPLIT == 2), "FP8 records");
   static_assert(MODE != kDecode || (FP8 && C == 1), "decode reads paged FP8 records, one row per team");
-  static_assert(MODE != kRowsMember || (WSPLIT == 1 && !V_IN_K), "membership: one-wave GQA teams");
+  static_assert(MODE != kRowsMember || C == 1, "membership: two-row, one-tile teams");
+  // membership bitmaps per workgroup: one pair per team
+  static constexpr int TEAMS_PER_WG = WSPLIT == 1 ? 4 : 1;
   static constexpr int KCH = KLDS ? KSTEPS / 4 : 0;   // 16-byte K chunks per slot per lane
   static constexpr int KROW = 64 * KSTEPS + 16;       // LDS row pitch (bytes): 16 (mod 32) * odd
   static constexpr int KLDS_BYTES = 16 * KROW;
@@ -281,19 +284,23 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   uint32_t* bmp = nullptr;
   int member_words = 0, member_base = 0;
   if constexpr (MEMBER) {
-    bmp = bmap_all + wv * 2 * kMemberWords;
+    // one wave marks both rows; a two-wave team marks one row per wave into
+    // the team's shared pair and meets at a barrier before either reads it
+    bmp = bmap_all + (WSPLIT == 1 ? wv : 0) * 2 * kMemberWords;
     const int b0 = __builtin_amdgcn_readlane(base_l, 0), b1 = __builtin_amdgcn_readlane(base_l, 1);
     const int n0 = __builtin_amdgcn_readlane(len_l, 0), n1 = __builtin_amdgcn_readlane(len_l, 1);
-    if (rows == 2 && b0 == b1 && n0 == n1 && n0 <= kMemberTokens) {
+    if (rows == 2 && b0 == b1 && n0 == n1 && n0 <= kMemberTokens) {   // team-uniform
       member_words = (n0 + 31) >> 5;
       member_base = b0;
-      for (int w = lane; w < 2 * kMemberWords; w += 64) {
+      constexpr int kRowsPerWave = WSPLIT == 1 ? 2 : 1;
+      const int r0 = WSPLIT == 1 ? 0 : split;
+      for (int w = lane; w < kRowsPerWave * kMemberWords; w += 64) {
         const int r = w >= kMemberWords;
-        if (w - r * kMemberWords < member_words) bmp[w] = 0u;
+        if (w - r * kMemberWords < member_words) bmp[r0 * kMemberWords + w] = 0u;
       }
       uint32_t dup = 0;
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
+      for (int r = r0; r < r0 + kRowsPerWave; ++r) {
         const int jr = __builtin_amdgcn_readlane(jmax_l, r);
         const int32_t* ir = p.idx + (int64_t)(t0 + r) * p.idx_row_stride;
         uint32_t* br = bmp + r * kMemberWords;
@@ -316,6 +323,12 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
         }
       }
       member = __ballot(dup != 0u) == 0;
+      if constexpr (WSPLIT > 1) {
+        // both rows marked, and both waves take the same decision
+        if (lane == 0) bmp[2 * kMemberWords + split] = member ? 0u : 1u;
+        __syncthreads();
+        member = (bmp[2 * kMemberWords] | bmp[2 * kMemberWords + 1]) == 0u;
+      }
     }
   }
 
@@ -849,7 +862,7 @@ attn_kernel(AttnParams p) {
   constexpr int QCAP = MODE == kRowsMember ? kMemberQueueCap : kQueueCap;
   __shared__ int32_t qtok[MODE == kUnion ? 1 : TT::WG_WAVES * QCAP];
   __shared__ uint32_t qbits[MODE == kUnion ? 1 : TT::WG_WAVES * QCAP];
-  __shared__ uint32_t bmap[MODE == kRowsMember ? TT::WG_WAVES * 2 * kMemberWords : 1];
+  __shared__ uint32_t bmap[MODE == kRowsMember ? TT::TEAMS_PER_WG * (2 * kMemberWords + 2) : 1];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int team = WSPLIT == 1 ? bid * 4 + w : bid;

@@ -25,7 +25,13 @@ hipError_t launch_slice(AttnParams p, int union_mode, hipStream_t stream) {
   } else {
     p.rows_per_team = r < 4 ? r : 4;
     if (!attn_grid<2>(p, kRows, &grid, &block)) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_kernel<576, 512, true, kRows, 1, 2, FP8, 2>), grid, block, 0, stream, p);
+    // two-row teams (5-8 heads) match their rows by membership
+    if (p.rows_per_team == 2)
+      hipLaunchKernelGGL((attn_kernel<576, 512, true, kRowsMember, 1, 2, FP8, 2>), grid, block, 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((attn_kernel<576, 512, true, kRows, 1, 2, FP8, 2>), grid, block, 0, stream,
+                         p);
   }
   return hipGetLastError();
 }
