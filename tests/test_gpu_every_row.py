@@ -80,16 +80,17 @@ def test_per_token_every_row(name, chunk):
     _report(m, f"{name} per-token ({entry})")
 
 
-def test_c1_shuffled_slots_every_row():
-    say("[every row] C1 with every row's slot order shuffled, through sparse_attn_chunk_prefill")
-    c = config("C1")
+@pytest.mark.parametrize("name,chunk", [("C1", True), ("C3", False), ("C3fp8", False)])
+def test_shuffled_slots_every_row(name, chunk):
+    say(f"[every row] {name} with every row's slot order shuffled (membership teams)")
+    c = config(name)
     sidx = gen.shuffle_slots(c.idx, 1)
     q, k, v, idx = _dev(c, sidx)
-    o, l = _host(*_per_token(c, q, k, v, idx, True))
+    o, l = _host(*_per_token(c, q, k, v, idx, chunk))
     a = _inputs(c, sidx)
     a.update(out=o, lse=l)
     m = oracle_pool.run("attn", a, _params(c), oracle_pool.row_chunks(c.num_rows))
-    _report(m, "C1 shuffled per-token")
+    _report(m, f"{name} shuffled per-token")
 
 
 @pytest.mark.parametrize("name,G", [("C1", 2), ("C3", 2), ("C3", 4), ("C3fp8", 2), ("C3fp8", 4),

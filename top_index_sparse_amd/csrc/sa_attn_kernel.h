@@ -60,9 +60,10 @@
 //   operands from there.
 //
 // Invalid slots (outside [0, kv_len), past topk or topk_len, or owned by
-// none of the team's rows) read a cache-resident 2 KB row of zeros and are
-// masked to -inf before the softmax; a tile with no valid slot for the team
-// is skipped whole. Workgroups are remapped so that each XCD (own L2)
+// none of the team's rows) read zeros (a row index the buffer descriptor's
+// range check rejects, or a cache-resident zero row on the 64-bit path) and
+// are masked to -inf before the softmax; a tile with no valid slot for the
+// team is skipped whole. Workgroups are remapped so that each XCD (own L2)
 // works on bands of consecutive rows, which share most of their slots.
 #pragma once
 
@@ -426,8 +427,8 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     return Tile{m0, (uint32_t)(bm >> (4 * slot_l)) & 0xfu};
   };
 
-  // Invalid slots load the zero row (their scores are forced to -inf, and
-  // their V is 0, multiplied by p = 0).
+  // Invalid slots load zeros (their scores are forced to -inf, and their V
+  // is 0, multiplied by p = 0).
   const uint32_t k_row_bytes = (uint32_t)(2 * p.k_row_stride);   // < 2^32 (host check)
   const uint32_t v_row_bytes = (uint32_t)(2 * p.v_row_stride);
   const bool v_like_k = v_row_bytes == k_row_bytes;
