@@ -28,14 +28,17 @@
 // of consecutive rows that share it, to be gathered with other queued tokens
 // as a tile of its own. Each row therefore sees each of its slots exactly
 // once (duplicates and ragged rows included), as in the per-token
-// definition. Union mode: the prebuilt union list with its ownership bits.
+// definition. Two-row teams of one request match by membership instead
+// (kRowsMember, below). Union mode: the prebuilt union list with its
+// ownership bits.
 //
 // Index lanes. Lane (g = l/16, m = l%16) reads the index of slot
 // 4g + m/4 of row m%4, so each quad of lanes holds one slot of all four rows
-// and compares them with quad DPP moves. The lane then turns its slot's
-// gathered token into K and V row byte offsets (one 32 x 32 -> 64-bit
-// multiply per stride for all 16 slots), and a DPP row broadcast hands slots
-// 4g..4g+3 to all sixteen lanes of group g.
+// and compares them with quad DPP moves. A DPP row broadcast then hands the
+// tokens of slots 4g..4g+3 to all sixteen lanes of group g, which gather
+// the rows through buffer descriptors (row index x stride + lane offset;
+// launches whose rows span more than 2 GiB, or whose strides do not fit the
+// descriptor, turn the token into a 64-bit byte offset instead).
 //
 // Products (MFMA operand layouts chosen so gathered bytes need no transpose):
 //   S^T[slot, col] = K_tile(16 x DQK) . Q^T(DQK x 16)       mfma 16x16x32 bf16
