@@ -8,10 +8,9 @@ namespace sa {
 namespace {
 
 // Waves per SIMD: two everywhere (the register budget of the products),
-// except the two-tile union team, which fits three (168 VGPRs, one
-// spilled); the third wave hides more of its per-tile latency (C2 union G=2
-// 1.76 -> 1.45 ms), where the per-token shapes lose more to spills than they
-// gain.
+// except the two-tile union team, which fits three (168 VGPRs, no spills);
+// the third wave hides more of its per-tile latency (C2 union G=2 1.76 ->
+// 1.45 ms), where the per-token shapes lose more to spills than they gain.
 template <int MODE, int C, int WSPLIT>
 hipError_t launch(const AttnParams& p, hipStream_t stream) {
   constexpr int kWaves = MODE == kUnion && C == 2 ? 3 : 2;

@@ -17,9 +17,10 @@ hipError_t launch_slice(AttnParams p, int union_mode, hipStream_t stream) {
     p.rows_per_team = r < p.G ? r : p.G;
     p.teams_per_group = (p.G + p.rows_per_team - 1) / p.rows_per_team;
     if (!attn_grid<2>(p, kUnion, &grid, &block)) return hipErrorInvalidConfiguration;
-    // FP8 union teams fit three waves per SIMD (168 VGPRs, 8 spilled), which
-    // hides more of their per-tile latency (C3 FP8 union G=2 0.48 -> 0.42
-    // ms); the bf16 union and per-token teams lose more to spills there
+    // FP8 union teams fit three waves per SIMD (168 VGPRs; 8 spilled, saved
+    // before the tile loop and reloaded after it), which hides more of their
+    // per-tile latency (C3 FP8 union G=2 0.48 -> 0.42 ms); the bf16 union and
+    // per-token teams lose more to spills there
     hipLaunchKernelGGL((attn_kernel<576, 512, true, kUnion, 1, 2, FP8, FP8 ? 3 : 2>), grid, block, 0,
                        stream, p);
   } else {
