@@ -403,3 +403,26 @@ def test_membership_groups_and_topk_len(group):
     out, lse = _run_prefill(case, dev, topk_len=i32_dev(tl))
     ro, rl = _oracle(case, topk_len=tl)
     check_close(out, lse, ro, rl, f"membership group {group} with topk_len")
+
+
+@pytest.mark.parametrize("scale", [1 / 16, 0.25, 0.5])
+@pytest.mark.parametrize("group,mla", [(6, False), (12, False), (8, True)])
+def test_large_score_ranges(scale, group, mla):
+    # Large sm_scale spreads the scores over hundreds of log2 units, so the
+    # running max moves (and the accumulators rescale) many times per row,
+    # and most probabilities underflow to 0; shuffled slots make the max
+    # arrive in any order.
+    say(f"[prefill] sm_scale {scale}, group {group}{' MLA' if mla else ''}, shuffled slots")
+    if mla:
+        case = gen.make_attn_case("small", seed=61, num_rows=29, kv_len=900, first_pos=880,
+                                  num_q_heads=group, num_kv_heads=1, head_dim_qk=576,
+                                  head_dim_v=512, topk=400, v_in_k=True, walk=True)
+    else:
+        case = _small(61, 29, 900, 880, group, 1, 400)
+    case.idx = gen.shuffle_slots(case.idx, 3)
+    case.scale = scale
+    dev = attn_to_dev(case)
+    out, lse = _run_prefill(case, dev)
+    ro, rl = _oracle(case)
+    e, el = check_close(out, lse, ro, rl, f"scale {scale}")
+    say(f"  max abs err O {e:.2e}  LSE {el:.2e}")
