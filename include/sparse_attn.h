@@ -354,6 +354,30 @@ sa_status indexer_topk(const float* scores, int64_t score_row_stride, const int3
                        int32_t num_rows, int32_t kv_len, int32_t k, int32_t* idx,
                        int64_t idx_row_stride, hipStream_t stream);
 
+/* FP8 MLA records to bf16 rows (PR 32779, "Accuracy Tests" (c): the kernel
+ * measured there reads rows that were dequantised to bf16 before it ran).
+ * For every token t < num_tokens with mask NULL or mask[t] != 0 and every KV
+ * head h < num_kv_heads, writes the 576 bf16 values of record (t, h) to
+ * out + t * out_row_stride + h * 576: latent value i as fp32(code_i) times
+ * its block scale, rounded to nearest-even bf16 (the reading every FP8
+ * attention path uses), then the 64 rope values unchanged. Other rows of
+ * out are not written, so a bf16 attention call over out gives the same
+ * result as the FP8 call over pool for index rows whose valid tokens are
+ * all marked. page_mark with src_page_tokens = 1 marks the tokens a step's
+ * index rows reference.
+ * pool  device uint8 [num_tokens][pool_row_stride] records (record layout
+ *       under SA_DTYPE_FP8_E4M3), pool_row_stride >= num_kv_heads * 656, a
+ *       multiple of 16
+ * mask  optional device int8 [num_tokens]
+ * out   device bf16 [num_tokens][out_row_stride] (elements), out_row_stride
+ *       >= num_kv_heads * 576, a multiple of 8; caller-owned
+ * One wavefront per (token, head), no workspace, no host read.
+ */
+sa_status sparse_attn_fp8_records_to_bf16(const uint8_t* pool, int64_t pool_row_stride,
+                                          int32_t num_tokens, int32_t num_kv_heads,
+                                          const int8_t* mask, void* out, int64_t out_row_stride,
+                                          hipStream_t stream);
+
 /* Host-only check of an attention descriptor, as sparse_attn_prefill (G=1)
  * or sparse_attn_prefill_union (G>1) would do before launching. Touches no
  * device. Returns SA_OK, SA_OK_FALLBACK (union tile illegal) or an error. */
@@ -375,7 +399,8 @@ typedef enum {
   SA_ENTRY_DECODE_PAGED = 7,
   SA_ENTRY_INDEXER_TOPK = 8,
   SA_ENTRY_DECODE_PAGED_NOALLOC = 9,
-  SA_ENTRY_COUNT = 10
+  SA_ENTRY_FP8_RECORDS_TO_BF16 = 10,
+  SA_ENTRY_COUNT = 11
 } sa_entry;
 uint64_t sa_call_count(int32_t entry);
 

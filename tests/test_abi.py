@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     for want in ("sparse_attn_prefill", "sparse_attn_chunk_prefill", "sparse_attn_prefill_union",
                  "sparse_attn_union_build", "sparse_attn_union_workspace_bytes", "page_mark",
                  "page_split", "sparse_attn_decode_paged", "sparse_attn_decode_workspace_bytes",
-                 "sparse_attn_decode_paged_noalloc",
+                 "sparse_attn_decode_paged_noalloc", "sparse_attn_fp8_records_to_bf16",
                  "indexer_topk",
                  "sa_validate_attn", "sa_last_error", "sa_call_count"):
         assert want in names
@@ -347,3 +347,24 @@ def test_indexer_topk_rejects_on_host():
     before = sa.sa_call_count("indexer_topk")
     assert f(None, 0, None, 0, 0, 5, None, 5, None) == 0                          # no rows
     assert sa.sa_call_count("indexer_topk") == before + 1
+
+
+def test_fp8_records_to_bf16_rejects_on_host():
+    f = sa.lib().sparse_attn_fp8_records_to_bf16
+
+    def call(pool=0x1000, ps=656, n=8, h=1, out=0x2000, os_=576):
+        return f(pool, ps, n, h, None, out, os_, None)
+
+    assert call(ps=655) == -2                 # shorter than a record
+    assert call(ps=664) == -2                 # not a multiple of 16
+    assert call(h=2, ps=1296) == -2           # two records need 1312 bytes
+    assert call(os_=570) == -2                # shorter than a row
+    assert call(os_=580) == -2                # not a multiple of 8
+    assert call(n=-1) == -2
+    assert call(h=0) == -2
+    assert call(pool=None) == -1
+    assert call(out=None) == -1
+    assert call(pool=0x1008) == -2            # misaligned
+    before = sa.sa_call_count("sparse_attn_fp8_records_to_bf16")
+    assert call(n=0, pool=None, out=None) == 0    # nothing to launch, counted
+    assert sa.sa_call_count("sparse_attn_fp8_records_to_bf16") == before + 1

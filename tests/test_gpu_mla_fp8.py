@@ -137,3 +137,60 @@ def test_mla_membership_teams_edge_cases(fp8):
                                   head_dim_v=512)
     e, el = check_close(out, lse, ro, rl, "MLA membership edge cases")
     say(f"  max abs err O {e:.2e}  LSE {el:.2e}")
+
+
+def _bf16_bits_to_f64(t):
+    return t.view(torch.int16).cpu().numpy().astype(np.uint16).astype(np.uint32) \
+        .__lshift__(16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("hkv,pad", [(1, 0), (2, 32)])
+def test_fp8_records_to_bf16_exact(hkv, pad):
+    # every converted value equals the oracle's dequantised bf16 value bit
+    # for bit; masked-off rows keep their previous contents
+    say(f"[fp8] records -> bf16 rows, {hkv} KV heads, strides padded by {pad}")
+    rng = np.random.default_rng(300 + hkv)
+    T = 777
+    rec = gen.mla_fp8_rows(rng, T * hkv).reshape(T, hkv, gen.FP8_ROW_BYTES)
+    pool = torch.zeros((T, hkv * 656 + pad), dtype=torch.uint8, device="cuda")
+    pool[:, :hkv * 656] = _u8_dev(rec).reshape(T, -1)
+    pv = pool[:, :hkv * 656].view(T, hkv, 656)
+    outb = torch.full((T, hkv * 576 + pad), -7.0, dtype=torch.bfloat16, device="cuda")
+    ov = outb[:, :hkv * 576].view(T, hkv, 576)
+    sa.fp8_records_to_bf16(pv, out=ov)
+    torch.cuda.synchronize()
+    want = oracle.mla_fp8_rows_to_f64(rec)
+    got = _bf16_bits_to_f64(ov.contiguous())
+    assert np.array_equal(got, want)
+    assert (outb[:, hkv * 576:] == -7.0).all()
+    # masked: only marked tokens are written
+    mask = torch.from_numpy((rng.random(T) < 0.3).astype(np.int8)).cuda()
+    outm = torch.full((T, hkv, 576), -7.0, dtype=torch.bfloat16, device="cuda")
+    sa.fp8_records_to_bf16(pv, mask=mask, out=outm)
+    torch.cuda.synchronize()
+    m = mask.cpu().numpy().astype(bool)
+    gm = _bf16_bits_to_f64(outm)
+    assert np.array_equal(gm[m], want[m])
+    assert (gm[~m] == -7.0).all()
+
+
+def test_fp8_staged_chain_matches_oracle():
+    # page_mark over one-token pages marks the tokens the index rows touch;
+    # the marked records are converted once; the bf16 MLA kernel then runs
+    # over the converted rows. Same definition as the FP8 kernels.
+    say("[fp8] staged chain: page_mark (one-token pages) -> records to bf16 -> bf16 prefill")
+    c = _small(81, 45, 3000, 2950, 8, 400)
+    c.idx[3, 5:9] = -1
+    c.idx[7, 2] = 5000
+    q, k, idx = bf16_dev(c.q), _u8_dev(c.k), i32_dev(c.idx)
+    mask = sa.page_mark(idx, c.kv_len, 1)
+    rows = torch.empty((c.kv_len, 1, 576), dtype=torch.bfloat16, device="cuda")
+    sa.fp8_records_to_bf16(k, mask=mask, out=rows)
+    out, lse = sa.sparse_attn_prefill(q, rows, None, idx, sm_scale=c.scale, head_dim_v=512)
+    fo, fl = sa.sparse_attn_prefill(q, k, None, idx, sm_scale=c.scale, head_dim_v=512)
+    torch.cuda.synchronize()
+    ro, rl = oracle.sparse_attention(c.q, _dec(c), None, c.idx, num_kv_heads=1, scale=c.scale,
+                                     kv_len=c.kv_len, head_dim_v=512)
+    check_close(out, lse, ro, rl, "staged fp8")
+    say(f"  staged vs in-kernel FP8: max |dO| {(out - fo).abs().max().item():.2e}, "
+        f"max |dLSE| {(lse - fl).abs().max().item():.2e}")

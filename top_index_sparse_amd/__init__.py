@@ -54,7 +54,7 @@ ENTRIES = {"sparse_attn_prefill": 0, "sparse_attn_chunk_prefill": 1,
            "sparse_attn_union_build": 2, "sparse_attn_prefill_union": 3,
            "page_mark": 4, "page_split": 5, "sparse_attn_chunk_prefill_union": 6,
            "sparse_attn_decode_paged": 7, "indexer_topk": 8,
-           "sparse_attn_decode_paged_noalloc": 9}
+           "sparse_attn_decode_paged_noalloc": 9, "sparse_attn_fp8_records_to_bf16": 10}
 SA_DECODE_SCRATCH_BYTES = 32 << 20
 
 
@@ -116,6 +116,7 @@ _SIGNATURES = {
                                         _I32, _P, _P, _I32, _P, _SZ, _P, _P, _P]),
     "sparse_attn_decode_paged_noalloc": (_I32, [ctypes.POINTER(AttnDesc), ctypes.POINTER(PageDesc),
                                                 _P, _P, _I32, _P, _P, _I32, _P, _P, _P]),
+    "sparse_attn_fp8_records_to_bf16": (_I32, [_P, _I64, _I32, _I32, _P, _P, _I64, _P]),
     "sa_validate_attn": (ctypes.c_int, [ctypes.POINTER(AttnDesc), _I32]),
     "sa_last_error": (ctypes.c_char_p, []),
     "sa_call_count": (ctypes.c_uint64, [_I32]),
@@ -422,6 +423,35 @@ def sparse_attn_chunk_prefill_union(q: torch.Tensor, k: torch.Tensor, v: Optiona
                                                ws.numel() * ws.element_size(), _ptr(out),
                                                _ptr(lse), _stream(stream))
     return out, lse, _check(st, "sparse_attn_chunk_prefill_union")
+
+
+def fp8_records_to_bf16(pool: torch.Tensor, *, mask: Optional[torch.Tensor] = None,
+                        out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """FP8 MLA records to bf16 rows (C: sparse_attn_fp8_records_to_bf16).
+
+    pool uint8 [tokens, Hkv, 656] (row stride free, a multiple of 16 bytes);
+    mask optional int8 [tokens] (rows with 0 are not written); out optional
+    bf16 [tokens, Hkv, 576] (row stride free). Returns out.
+    """
+    _need(pool, "pool", torch.uint8, 3)
+    if pool.shape[2] != 656:
+        raise ValueError(f"pool records are 656 bytes, got {pool.shape[2]}")
+    _rows_dense(pool, "pool")
+    T, H = pool.shape[0], pool.shape[1]
+    if out is None:
+        out = torch.empty((T, H, 576), dtype=torch.bfloat16, device=pool.device)
+    _need(out, "out", torch.bfloat16, 3, pool.device)
+    _need_size(out, "out", T, (H, 576))
+    _rows_dense(out, "out")
+    if mask is not None:
+        _need(mask, "mask", torch.int8, 1, pool.device)
+        if mask.shape[0] < T or not mask.is_contiguous():
+            raise ValueError("mask must be a contiguous int8 tensor of at least tokens entries")
+    st = lib().sparse_attn_fp8_records_to_bf16(
+        _ptr(pool), pool.stride(0) if T else H * 656, T, H, _ptr(mask), _ptr(out),
+        out.stride(0) if T else H * 576, _stream(stream))
+    _check(st, "sparse_attn_fp8_records_to_bf16")
+    return out
 
 
 def page_mark(idx: torch.Tensor, num_src_pages: int, src_page_tokens: int, *,

@@ -617,6 +617,36 @@ sa_status indexer_topk(const float* scores, int64_t score_row_stride, const int3
   return ok(SA_ENTRY_INDEXER_TOPK);
 }
 
+sa_status sparse_attn_fp8_records_to_bf16(const uint8_t* pool, int64_t pool_row_stride,
+                                          int32_t num_tokens, int32_t num_kv_heads,
+                                          const int8_t* mask, void* out, int64_t out_row_stride,
+                                          hipStream_t stream) {
+  g_err[0] = 0;
+  if (num_tokens < 0 || num_kv_heads <= 0)
+    return fail(SA_ERR_SHAPE, "num_tokens %d, num_kv_heads %d", num_tokens, num_kv_heads);
+  if (pool_row_stride < (int64_t)num_kv_heads * 656 || pool_row_stride % 16)
+    return fail(SA_ERR_SHAPE, "pool_row_stride %lld: at least %d bytes and a multiple of 16",
+                (long long)pool_row_stride, num_kv_heads * 656);
+  if (out_row_stride < (int64_t)num_kv_heads * 576 || out_row_stride % 8)
+    return fail(SA_ERR_SHAPE, "out_row_stride %lld: at least %d elements and a multiple of 8",
+                (long long)out_row_stride, num_kv_heads * 576);
+  if (num_tokens == 0) return ok(SA_ENTRY_FP8_RECORDS_TO_BF16);
+  if (!pool || !out) return fail(SA_ERR_NULL, "pool and out are required");
+  if ((reinterpret_cast<uintptr_t>(pool) & 15u) || (reinterpret_cast<uintptr_t>(out) & 15u))
+    return fail(SA_ERR_SHAPE, "pool and out must be 16-byte aligned");
+  sa::Fp8RowsParams p{};
+  p.pool = pool;
+  p.pool_row_stride = pool_row_stride;
+  p.mask = mask;
+  p.out = static_cast<uint16_t*>(out);
+  p.out_row_stride = out_row_stride;
+  p.rows = (int64_t)num_tokens * num_kv_heads;
+  p.num_kv_heads = num_kv_heads;
+  const hipError_t e = sa::launch_fp8_records_to_bf16(p, stream);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok(SA_ENTRY_FP8_RECORDS_TO_BF16);
+}
+
 sa_status page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src_pages,
                     int32_t src_page_tokens, int8_t* mask, hipStream_t stream) {
   g_err[0] = 0;

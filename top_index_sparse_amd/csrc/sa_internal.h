@@ -154,6 +154,17 @@ hipError_t launch_page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src
 hipError_t launch_page_split(const PageParams& p, hipStream_t stream);
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream);
 
+struct Fp8RowsParams {
+  const uint8_t* pool;
+  int64_t pool_row_stride;   // bytes
+  const int8_t* mask;        // nullable
+  uint16_t* out;
+  int64_t out_row_stride;    // elements
+  int64_t rows;              // num_tokens * num_kv_heads
+  int32_t num_kv_heads;
+};
+hipError_t launch_fp8_records_to_bf16(const Fp8RowsParams& p, hipStream_t stream);
+
 // sa_api.cpp: the decode entry points' common body (counted under `entry`
 // on success). Without `scratch` it runs over the caller's `ws`; with it,
 // once every argument has passed, over the static scratch of `ws_bytes`

@@ -20,15 +20,38 @@ __global__ void __launch_bounds__(kThreads) page_clear_kernel(int8_t* mask, int3
   if (i < n) mask[i] = 0;
 }
 
-// One thread per index: same-value stores of 1, no atomics needed.
+// Sixteen indices per thread (four 16-byte loads in flight where the array
+// is 16-byte aligned): same-value stores of 1, no atomics needed. A store is skipped
+// when the byte already reads 1, so that many indices into few pages (a
+// prefill step's rows over one-token pages) do not all write the same lines.
+// page_shift >= 0: src_page_tokens is 1 << page_shift.
+constexpr int kMarkPerThread = 16;
+
 __global__ void __launch_bounds__(kThreads) page_mark_kernel(const int32_t* idx, int64_t num_idx,
                                                              int64_t pool_tokens,
                                                              int32_t src_page_tokens,
+                                                             int32_t page_shift, bool vec16,
                                                              int8_t* mask) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= num_idx) return;
-  const int32_t t = idx[i];
-  if (t >= 0 && (int64_t)t < pool_tokens) mask[t / src_page_tokens] = 1;
+  const int64_t i0 = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * kMarkPerThread;
+  if (i0 >= num_idx) return;
+  int32_t t[kMarkPerThread];
+  if (vec16 && i0 + kMarkPerThread <= num_idx) {
+    u32x4_t v[kMarkPerThread / 4];
+#pragma unroll
+    for (int q = 0; q < kMarkPerThread / 4; ++q) v[q] = ld16(idx + i0 + 4 * q);
+#pragma unroll
+    for (int j = 0; j < kMarkPerThread; ++j) t[j] = (int32_t)v[j / 4][j % 4];
+  } else {
+#pragma unroll
+    for (int j = 0; j < kMarkPerThread; ++j) t[j] = i0 + j < num_idx ? idx[i0 + j] : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < kMarkPerThread; ++j) {
+    if (t[j] >= 0 && (int64_t)t[j] < pool_tokens) {
+      int8_t* m = mask + (page_shift >= 0 ? t[j] >> page_shift : t[j] / src_page_tokens);
+      if (*m == 0) *m = 1;
+    }
+  }
 }
 
 // Copies n bytes; sixteen 16-byte loads per thread are issued before their
@@ -82,9 +105,14 @@ hipError_t launch_page_mark(const int32_t* idx, int64_t num_idx, int32_t num_src
                      dim3(kThreads), 0, stream, mask, num_src_pages);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || num_idx == 0) return e;
-  hipLaunchKernelGGL(page_mark_kernel, dim3((unsigned)((num_idx + kThreads - 1) / kThreads)),
+  const int32_t shift = (src_page_tokens & (src_page_tokens - 1)) == 0
+                            ? __builtin_ctz((uint32_t)src_page_tokens) : -1;
+  const bool vec16 = (reinterpret_cast<uintptr_t>(idx) & 15) == 0;
+  const int64_t per_block = (int64_t)kThreads * kMarkPerThread;
+  hipLaunchKernelGGL(page_mark_kernel, dim3((unsigned)((num_idx + per_block - 1) / per_block)),
                      dim3(kThreads), 0, stream, idx, num_idx,
-                     (int64_t)num_src_pages * src_page_tokens, src_page_tokens, mask);
+                     (int64_t)num_src_pages * src_page_tokens, src_page_tokens, shift, vec16,
+                     mask);
   return hipGetLastError();
 }
 
