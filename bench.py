@@ -25,6 +25,12 @@ L1 tag access per clock per CU, 64 B each for these loads, x 256 CUs x
 bytes per call that rocprofv3 counters measured on the current kernel
 source (null when the source has changed since).
 
+`others` times every other workload the same way: C2 (group 12 over two KV
+heads), MLA per-token and union G=2/4 (C3), MLA over FP8 records with the
+dequant in the kernel and staged (records converted to bf16 rows once per
+call), the ragged C4 chunk prefill and its union, the indexer top-k and the
+chains over its rows, and the decode step (page mark, masked split, decode).
+
 The CPU baseline runs the fp64 oracle on every row of the same workload
 (`--cpu-stride N`: every N-th row), in worker processes forked before the
 GPU is touched, and its results double as a parity gate on those rows.
