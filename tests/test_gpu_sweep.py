@@ -2,8 +2,9 @@
 points (per-token, ragged chunk prefill, union, union over ragged requests),
 both head shapes and both K encodings, against the fp64 oracle. Each case
 draws its own group size, row count (tails not a multiple of any team or
-group), top-k, KV length, padded strides, top-k lengths, duplicates, -1 and
-out-of-range indices."""
+group), top-k, KV length, padded strides, top-k lengths, -1 and
+out-of-range indices; odd cases also hold a duplicated index in every row
+(even cases let two-row teams match their rows by membership)."""
 import numpy as np
 import pytest
 import torch
@@ -48,8 +49,8 @@ def _case(i):
     m = rng.random(idx.shape)
     idx[m < 0.05] = -1
     idx[(m >= 0.05) & (m < 0.08)] = kv + rng.integers(0, 50)
-    if topk > 3:
-        idx[:, 1] = idx[:, 0]
+    if topk > 3 and i % 2:
+        idx[:, 1] = idx[:, 0]   # (odd cases: two-row teams then match by position)
     c.idx = idx.astype(np.int32)
     return rng, c, mla, fp8
 
