@@ -658,22 +658,28 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
       float s2[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) s2[i] = keep_if_bit(st[c][i], own[i], col_sh[c]);
-      float mx = max4(s2[0], s2[1], s2[2], s2[3]);
-      mx = rows_max4(mx) * sc;
-      const float m_new = mx > m_run[c] + kSlack ? mx : m_run[c];
-      float pr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(s2[i], sc, -m_new));
-      // Rescale only when some column's reference max moved (alpha == 1
-      // elsewhere).
-      if (__builtin_amdgcn_ballot_w64(m_new != m_run[c])) {
+      // The reference max moves only when some score of the column passes
+      // it by more than kSlack. Each lane tests its own four scores first
+      // (rounding is monotonic, so some lane passes iff the column's max
+      // does); the cross-lane max runs only when some lane of the wave
+      // passes, which after a column's first tiles is rare.
+      const float mx = max4(s2[0], s2[1], s2[2], s2[3]);
+      const float m_lim = m_run[c] + kSlack;
+      if (__builtin_amdgcn_ballot_w64(mx * sc > m_lim)) {
+        const float cm = rows_max4(mx) * sc;
+        const float m_new = cm > m_lim ? cm : m_run[c];
+        // rescale where the column's reference max moved (alpha == 1
+        // elsewhere)
         const float alpha = fast_exp2(m_run[c] - m_new);
         l_run[c] *= alpha;
 #pragma unroll
         for (int mt = 0; mt < MTILES; ++mt) acc[c][mt] *= alpha;
+        m_run[c] = m_new;
       }
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(s2[i], sc, -m_run[c]));
       l_run[c] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-      m_run[c] = m_new;
       pop[c] = __builtin_bit_cast(i16x4_t,
                                   (u32x2_t){pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])});
     }
