@@ -109,3 +109,30 @@ def test_topk_sweep(i):
     rl = rng.integers(-5, kv + 20, T).astype(np.int32) if rng.random() < 0.6 else None
     say(f"[topk sweep {i}] T={T} kv={kv} k={k} kind={kind} row_len={rl is not None}")
     _check(s, k, rl, f"sweep {i}")
+
+
+def _sample_positions(kv):
+    """Positions the sampled selection reads for its threshold (rows of
+    4097 .. 32768 positions): thread j of the row's 1024 reads position
+    4 (c 1024 + j) with c = j mod (chunks of 4096 positions)."""
+    nch = 8 if kv > 16384 else 4
+    j = np.arange(1024)
+    return 4 * ((j % nch) * 1024 + j)
+
+
+@pytest.mark.parametrize("kv", [16384, 32768])
+def test_topk_sample_misleads(kv):
+    """The sample sees only planted large scores, so its threshold keeps
+    fewer than k elements; the row must fall back to the full selection."""
+    say(f"[topk] kv {kv}: large scores planted where the threshold sample reads")
+    rng = np.random.default_rng(kv + 3)
+    s = rng.standard_normal((4, kv)).astype(np.float32)
+    pos = _sample_positions(kv)
+    s[0, pos] = 100.0
+    s[1, pos] = np.float32(5.0) + rng.random(pos.size).astype(np.float32)
+    s[2, pos[::2]] = 7.0                       # half the sample
+    s[3, pos] = -100.0                         # the sample sees only small scores
+    for k in (1, 600, 1024, 1025, 2051, 4096):
+        _check(s, k, None, f"kv={kv} k={k} planted")
+        _check(s, k, np.array([kv, kv - 5, kv // 2 + 3, 4 * k // 3 + 1], np.int32),
+               f"kv={kv} k={k} planted, lengths")

@@ -7,10 +7,24 @@
 // gfx950 design: one 1024-thread workgroup per row, two resident per CU.
 //   Keys. A score's bits map to a uint32 key whose unsigned order is the
 //   float order (-0 is folded onto +0 first, so the two tie).
-//   Level 0. An LDS histogram of the keys' top 13 bits (8192 bins, wide
-//   enough that scores crowding a few exponents still spread their atomics)
-//   and a block-wide scan from the top bin down find the bin b0 that holds
-//   the k-th largest key.
+//   Sampled selection (rows of 4097 .. 32768 positions, k <= 4096, the
+//   row's raw bits held in registers). A 1024-element strided sample of
+//   the row gives a lower bound on its k-th largest key: the 11-bit bin
+//   holding the sample's r-th largest, r the expected rank plus four
+//   standard deviations. One compare per element (the raw bits compared as
+//   signed integers when the bound is above +0) sends every element at or
+//   above the bound to an LDS list, compacted by wave ballots; the exact
+//   selection then runs on that list alone: levels of 11 bits over the
+//   keys relative to the bound, until the threshold bin is either needed
+//   whole or small enough (at most 64) for one wave to rank its members by
+//   key and position. A list that misses the k-th largest or overflows
+//   sends the row to the full path below, so the result never depends on
+//   the sample. Against the full path it takes no histogram atomics for
+//   the row's elements, and about a third of their instructions.
+//   Full path. Level 0: an LDS histogram of the keys' top 13 bits (8192
+//   bins, wide enough that scores crowding a few exponents still spread
+//   their atomics) and a block-wide scan from the top bin down find the bin
+//   b0 that holds the k-th largest key.
 //   Classes. Every element is then above b0 (kept, into an LDS bitmap by
 //   position), in b0 (a candidate) or below (dropped). Candidates, usually a
 //   few hundred, are appended to an LDS list straight from the registers;
@@ -33,6 +47,8 @@
 //   totals.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "sa_device.h"
 #include "sa_internal.h"
@@ -346,6 +362,295 @@ struct FastLds : TopkLds {
   int32_t cpos[kCand];
 };
 
+// ---- sampled selection (rows held in registers, k <= kSampleMaxK) -------------
+// A row's k-th largest key is bracketed from below by a threshold read off a
+// sample of the row: every element at or above it goes to a candidate list
+// (one compare per element, no atomics), and the exact selection runs on
+// that list alone. The threshold is the bin (the key's top 11 bits) holding
+// the sample's r-th largest key, r the expected rank of the row's k-th
+// largest in the sample plus four standard deviations; whenever the list
+// turns out to miss the k-th largest (fewer than k candidates) or to
+// overflow, the row takes the full path instead, so the result never
+// depends on the sample.
+constexpr int kLevelBins = 2048;   // 11 bits per level
+constexpr int kSCap = 6144;        // candidate list capacity (about k + 30 % in practice)
+constexpr int kSampleMaxK = 4096;
+constexpr int kSmall = 64;         // a bin this small is ranked by one wave
+
+template <int PER>
+struct SampledLds {
+  static constexpr int kWords = PER * kThreads / 32;
+  // (the list first: its stores' constant offsets fold into the instruction)
+  uint32_t craw[kSCap];           // candidates: raw score bits
+  uint32_t cpos[kSCap];           // and positions
+  uint32_t hist[2][kLevelBins];   // [0]: the sample; then the levels alternate [1], [0], [1]
+  uint32_t selb[kWords];          // kept, by position
+  uint32_t tieb[kWords];          // tied at the final threshold, by position
+  uint32_t red2[2 * kWaves];
+  uint32_t ncand;
+  uint32_t hi;                    // the row's largest key (a bound, below +0)
+  uint32_t found[4];
+  uint32_t nsmall;                // a threshold bin of at most kSmall candidates, ranked whole
+  uint32_t skey[kSmall];
+  uint32_t spos[kSmall];
+};
+
+// Largest value over the wave's lanes, in lane 63 (DPP steps as wave_scan64).
+__device__ __forceinline__ uint32_t wave_max64(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true));   // row_shr:1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true));   // row_shr:2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true));   // row_shr:4
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true));   // row_shr:8
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// One wave: over nb bins of h (a power of two, at most 2048), with need
+// = need_of(total count), the bin holding the need-th largest counted from
+// the top bin down. found: the bin, how many of it are needed, whether that
+// is all of it. Lane l sums bins [nb - per (l+1), nb - per l); the lane
+// holding the need-th then has its bins spread over the wave.
+template <int UNROLL, typename NeedOf>
+__device__ __forceinline__ void wave_find(const uint32_t* h, int nb, NeedOf need_of, uint32_t* found) {
+  const int lane = threadIdx.x & 63;
+  const int per = nb >= 64 ? nb >> 6 : 1;
+  const int top = nb - per * lane;
+  uint32_t s = 0;
+  if (top > 0) {
+    if (per >= 4) {
+      // UNROLL reads in flight (one where the row's keys still hold 32 registers)
+#pragma unroll UNROLL
+      for (int j = 0; j < per; j += 4) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(h + top - per + j);
+        s += (v[0] + v[1]) + (v[2] + v[3]);
+      }
+    } else {
+      for (int j = 0; j < per; ++j) s += h[top - 1 - j];
+    }
+  }
+  const uint32_t incl = wave_scan64(s);
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  uint32_t need = need_of(total);   // 1 <= need <= total
+  need = need < total ? need : total;   // (so that both searches below find a lane)
+  const int L = __builtin_ctzll(__ballot(incl >= need));
+  const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)incl, L) -
+                         (uint32_t)__builtin_amdgcn_readlane((int)s, L);
+  const int topL = nb - per * L;
+  const uint32_t c = lane < per ? h[topL - 1 - lane] : 0u;
+  const uint32_t incl2 = wave_scan64(c);
+  const int M = __builtin_ctzll(__ballot(lane < per && above + incl2 >= need));
+  const uint32_t cM = (uint32_t)__builtin_amdgcn_readlane((int)c, M);
+  const uint32_t before = above + (uint32_t)__builtin_amdgcn_readlane((int)incl2, M) - cM;
+  if (lane == 0) {
+    found[0] = (uint32_t)(topL - 1 - M);
+    found[1] = need - before;
+    found[2] = cM == need - before;
+    found[3] = cM;
+  }
+}
+
+// The sampled selection of a row of n > k positions whose raw score bits
+// sit in kreg, 0xffffffff at every position past the row (no score has
+// those bits). Marks the kept positions in
+// S.selb and the ties at the final threshold in S.tieb, sets *tie_need,
+// and returns true; when the row needs the full path, runs full() once S
+// is free for reuse and returns false. (full() is called here rather than
+// by the caller so that no path out of the sampled selection still holds
+// the row's registers.)
+template <int PER, typename Full>
+__device__ __forceinline__ bool sampled_select(SampledLds<PER>& S, int n, uint32_t k,
+                                               const uint32_t* kreg, uint32_t* tie_need,
+                                               Full&& full) {
+  constexpr int NCH = PER / 4;
+  constexpr int NWORDS = SampledLds<PER>::kWords;
+  constexpr int E = kSCap / kThreads;   // list entries per thread
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint32_t* flat = &S.hist[0][0];
+  for (int b = tid; b < 2 * kLevelBins; b += kThreads) flat[b] = 0u;
+  for (int w = tid; w < NWORDS; w += kThreads) S.selb[w] = S.tieb[w] = 0u;
+  if (tid == 0) {
+    S.ncand = 0u;
+    S.hi = 0u;
+    S.nsmall = 0u;
+  }
+  // sample: position 4 (c kThreads + tid) of chunk c = tid mod NCH
+  const int cs = tid & (NCH - 1);
+  // (each value passes through an empty asm, so the selects stay selects
+  // rather than becoming an indexed read that would move kreg to memory)
+  uint32_t sraw = kreg[0];
+#pragma unroll
+  for (int i = 1; i < NCH; ++i) {
+    uint32_t v = kreg[4 * i];
+    asm("" : "+v"(v));
+    sraw = cs == i ? v : sraw;
+  }
+  const uint32_t skey = 4 * (cs * kThreads + tid) < n ? score_key(sraw) : 0u;
+  __syncthreads();
+  if (skey) atomicAdd(&S.hist[0][skey >> 21], 1u);
+  __syncthreads();
+  if (wv == 0) {
+    const float pk = (float)k / (float)n;
+    wave_find<1>(S.hist[0], kLevelBins, [&](uint32_t ns) {
+      const float mean = (float)ns * pk;
+      const uint32_t r = (uint32_t)ceilf(mean + 4.f * sqrtf(mean * (1.f - pk)) + 4.f);
+      return r < ns ? r : ns;
+    }, S.found);
+  }
+  __syncthreads();
+  uint32_t tk = S.found[0] << 21;
+  tk = tk ? tk : 1u;   // (0 keys are past the row)
+  for (int b = tid; b < kLevelBins; b += kThreads) S.hist[0][b] = 0u;   // for the second level
+
+  // ---- candidates: every element with key >= tk --------------------------
+  // Above +0 the key order of the raw bits is their signed order, so one
+  // compare decides; otherwise the key is formed first.
+  // A bound on the largest key of the row comes out of the same pass: above
+  // +0 the largest raw bits read as signed (the row's largest key itself);
+  // otherwise the largest key there is (at most one more level).
+  uint32_t top = 0xffffffffu;
+  auto filter = [&](auto above_zero) {
+    const int32_t tr = (int32_t)(tk ^ 0x80000000u);
+    int32_t mraw = -1;
+#pragma unroll
+    for (int g = 0; g < NCH / 2; ++g) {   // two chunks per list allocation
+      bool in[8];
+      uint64_t bal[8];
+      uint32_t tot = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t raw = kreg[8 * g + j];
+        if constexpr (decltype(above_zero)::value) {
+          in[j] = (int32_t)raw >= tr;
+          mraw = max(mraw, (int32_t)raw);
+        } else {
+          in[j] = score_key(raw) >= tk;
+        }
+        bal[j] = __builtin_amdgcn_ballot_w64(in[j]);
+        tot += (uint32_t)__popcll(bal[j]);
+      }
+      if (tot) {   // wave-uniform
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&S.ncand, tot);
+        base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+        if (base + tot <= (uint32_t)kSCap) {   // else the list overflows: the full path
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if (in[j]) {
+              // (the wave's base stays scalar: one shift-add forms the address)
+              const uint32_t below = __builtin_amdgcn_mbcnt_hi(
+                  (uint32_t)(bal[j] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
+              S.craw[base + below] = kreg[8 * g + j];
+              S.cpos[base + below] = (uint32_t)(4 * ((2 * g + (j >> 2)) * kThreads + tid) + (j & 3));
+            }
+            base += (uint32_t)__popcll(bal[j]);
+          }
+        }
+      }
+    }
+    if constexpr (decltype(above_zero)::value) top = mraw < 0 ? 0u : (uint32_t)mraw | 0x80000000u;
+  };
+  if (tk > 0x80000000u) filter(std::true_type{});
+  else filter(std::false_type{});
+  top = wave_max64(top);
+  if (lane == 0) atomicMax(&S.hi, top);
+  __syncthreads();
+  const uint32_t nc = S.ncand;
+  if (nc < k || nc > (uint32_t)kSCap) {   // uniform
+    __syncthreads();   // every thread has read ncand before the memory is reused
+    full();
+    return false;
+  }
+
+  // ---- exact selection on the list: keys relative to tk, 11 bits a level -----
+  const uint32_t hi = S.hi - tk;   // (S.hi >= tk: the row's largest key is a candidate)
+  uint32_t rk[E];
+  int32_t rp[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t c = (uint32_t)(tid + e * kThreads);
+    rk[e] = 0u;
+    rp[e] = -1;
+    if (c < nc) {
+      rk[e] = score_key(S.craw[c]) - tk;
+      rp[e] = (int32_t)S.cpos[c];
+    }
+  }
+  const int nbits = hi ? 32 - __builtin_clz(hi) : 0;   // every relative key is below 2^nbits
+  int sp = nbits;                                      // bits at and above sp: the prefix P
+  int s = nbits > 11 ? nbits - 11 : 0;
+  uint32_t P = 0, need = k;
+  int hb = 1;
+  while (true) {
+    const int nb = 1 << (sp - s);
+    uint32_t* h = S.hist[hb];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (rp[e] >= 0 && (sp >= 32 || (rk[e] >> sp) == P))
+        atomicAdd(&h[(rk[e] >> s) & (uint32_t)(nb - 1)], 1u);
+    __syncthreads();
+    if (wv == 0) wave_find<4>(h, nb, [&](uint32_t) { return need; }, S.found);
+    __syncthreads();
+    const uint32_t bin = S.found[0];
+    need = S.found[1];
+    const bool whole = S.found[2] != 0u;
+    const uint32_t cnt = S.found[3];
+    for (int b = tid; b < nb; b += kThreads) h[b] = 0u;   // (read only before the barrier)
+    P = (sp >= 32 ? 0u : P << (sp - s)) | bin;
+    sp = s;
+    if (whole || s == 0) break;
+    if (cnt <= (uint32_t)kSmall) {   // uniform
+      // Everything above the bin is kept; the bin's cnt candidates are ranked
+      // by one wave (larger key first, then lower position) and the first
+      // `need` of them kept: no further level.
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (rp[e] >= 0) {
+          const uint32_t pk = rk[e] >> sp;
+          if (pk > P) {
+            atomicOr(&S.selb[rp[e] >> 5], 1u << (rp[e] & 31));
+          } else if (pk == P) {
+            const uint32_t at = atomicAdd(&S.nsmall, 1u);   // < cnt <= kSmall
+            S.skey[at] = rk[e];
+            S.spos[at] = (uint32_t)rp[e];
+          }
+        }
+      }
+      __syncthreads();
+      if (wv == 0) {
+        const uint32_t key = lane < (int)cnt ? S.skey[lane] : 0u;
+        const uint32_t pos = lane < (int)cnt ? S.spos[lane] : 0u;
+        uint32_t rank = 0;
+        for (int j = 0; j < (int)cnt; ++j) {
+          const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)key, j);
+          const uint32_t pj = (uint32_t)__builtin_amdgcn_readlane((int)pos, j);
+          rank += (kj > key || (kj == key && pj < pos)) ? 1u : 0u;
+        }
+        if (lane < (int)cnt && rank < need) atomicOr(&S.selb[pos >> 5], 1u << (pos & 31));
+      }
+      *tie_need = 0;
+      __syncthreads();
+      return true;
+    }
+    s = s > 11 ? s - 11 : 0;
+    hb ^= 1;
+  }
+  // kept above the final prefix, tied at it
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (rp[e] >= 0) {
+      const uint32_t pk = sp >= 32 ? 0u : rk[e] >> sp;
+      const uint32_t bit = 1u << (rp[e] & 31);
+      if (pk > P) atomicOr(&S.selb[rp[e] >> 5], bit);
+      else if (pk == P) atomicOr(&S.tieb[rp[e] >> 5], bit);
+    }
+  }
+  *tie_need = need;
+  __syncthreads();
+  return true;
+}
+
 // Every row's visible length and, when it exceeds k, the selection.
 __device__ __forceinline__ int row_length(const TopkParams& p, int t) {
   int n = p.kv_len;
@@ -358,9 +663,19 @@ __device__ __forceinline__ int row_length(const TopkParams& p, int t) {
 
 // One workgroup per row. REG: the row's scores are read once into
 // registers, all chunks requested before the first is used.
-template <int PER, bool REG>
-__global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
-  __shared__ FastLds<PER> L;
+// Two rows per CU: 8 waves per SIMD, which bounds both register files.
+template <int PER, bool REG, bool SAMPLED = false>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+topk_fast_kernel(TopkParams p) {
+  // SAMPLED (rows in registers, k <= kSampleMaxK): the sampled selection
+  // first, the full path only where it gives up; the two share the memory
+  static_assert(!SAMPLED || REG, "the sampled selection reads the row from registers");
+  union Lds {
+    FastLds<PER> f;
+    typename std::conditional<SAMPLED, SampledLds<PER>, TopkLds>::type s;
+  };
+  __shared__ Lds U;
+  FastLds<PER>& L = U.f;
   constexpr int NCH = PER / 4;                      // 4096-position chunks
   // chunks per group: re-read groups are loaded whole before their first use
   constexpr int GCH = REG ? (NCH < 8 ? NCH : 8) : 4;
@@ -399,6 +714,14 @@ __global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) k4[c] = REG ? kreg[4 * i + c] : kg[4 * (i % GCH) + c];
   };
+  uint32_t tie_need = 0;
+  auto full_path = [&]() {
+  if constexpr (SAMPLED) {
+    // (keeps the key conversion below from being hoisted above the sampled
+    // selection, where raw bits and keys would hold registers together)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) asm volatile("" : "+v"(kreg[i]));
+  }
   uint32_t need = (uint32_t)p.k, b0 = 0;
   bool whole0 = true;
 
@@ -501,7 +824,6 @@ __global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
   __syncthreads();
 
   // ---- levels 1 and 2 on the candidates (or, on overflow, the row) ---------
-  uint32_t tie_need = 0;
   if (!whole0) {
     const uint32_t nc = L.ncand;
     const bool spill = nc > (uint32_t)kCand;   // candidates overflow their list
@@ -560,6 +882,23 @@ __global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
     __syncthreads();
   }
 
+  };   // full path
+  bool sampled = false;
+  if constexpr (SAMPLED) {
+    // the chunk that reaches the row's end: its positions past n (a 16-byte
+    // read may cover them) become 0xffffffff, like the chunks wholly past it
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      if (4 * i * kThreads < n && 4 * (i + 1) * kThreads > n) {   // uniform
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          kreg[4 * i + c] = 4 * (i * kThreads + tid) + c < n ? kreg[4 * i + c] : 0xffffffffu;
+      }
+    }
+    sampled = sampled_select<PER>(U.s, n, (uint32_t)p.k, kreg, &tie_need, full_path);
+  }
+  else full_path();
+
   // ---- output from the bitmaps, in position order ----------------------------
   // An element goes to (kept before it) + min(tied before it, tie_need); a
   // tie is kept while fewer than tie_need ties precede it.
@@ -567,13 +906,28 @@ __global__ void __launch_bounds__(kThreads) topk_fast_kernel(TopkParams p) {
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
     const int w = tid * WPT + j;
-    ksel[j] = w < NWORDS ? (L.amap[w] | L.selb[w]) : 0u;
-    ktie[j] = w < NWORDS ? L.tieb[w] : 0u;
+    uint32_t sw = 0, tw = 0;
+    if (w < NWORDS) {
+      sw = L.amap[w] | L.selb[w];
+      tw = L.tieb[w];
+      if constexpr (SAMPLED) {
+        if (sampled) {
+          sw = U.s.selb[w];
+          tw = U.s.tieb[w];
+        }
+      }
+    }
+    ksel[j] = sw;
+    ktie[j] = tw;
     ns += __popc(ksel[j]);
     nt += __popc(ktie[j]);
   }
   uint32_t kept, tied, ts, tt;
-  block_exclusive_scan2(tid, ns, nt, L.red2, &kept, &tied, &ts, &tt);
+  uint32_t* red2 = L.red2;
+  if constexpr (SAMPLED) {
+    if (sampled) red2 = U.s.red2;
+  }
+  block_exclusive_scan2(tid, ns, nt, red2, &kept, &tied, &ts, &tt);
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
     const int w = tid * WPT + j;
@@ -614,10 +968,15 @@ __global__ void __launch_bounds__(kThreads) topk_generic_kernel(TopkParams p) {
 hipError_t launch_topk(const TopkParams& p, hipStream_t stream) {
   const int kv = p.kv_len;
   const dim3 grid((unsigned)p.num_rows), block(kThreads);
+  const bool sampled = p.k <= kSampleMaxK;
   if (kv <= 4 * kThreads)
     hipLaunchKernelGGL((topk_fast_kernel<4, true>), grid, block, 0, stream, p);
+  else if (kv <= 16 * kThreads && sampled)
+    hipLaunchKernelGGL((topk_fast_kernel<16, true, true>), grid, block, 0, stream, p);
   else if (kv <= 16 * kThreads)
     hipLaunchKernelGGL((topk_fast_kernel<16, true>), grid, block, 0, stream, p);
+  else if (kv <= 32 * kThreads && sampled)
+    hipLaunchKernelGGL((topk_fast_kernel<32, true, true>), grid, block, 0, stream, p);
   else if (kv <= 32 * kThreads)
     hipLaunchKernelGGL((topk_fast_kernel<32, true>), grid, block, 0, stream, p);
   else if (kv <= 64 * kThreads)
