@@ -695,6 +695,22 @@ def main():
     copy_gbs = 2.0 * (1 << 30) / (copy_ms * 1e-3) / 1e9
     del csrc, cdst
 
+    # The gather stream alone (sa_probe_gather: the same 16-byte K/V row
+    # reads through the same descriptors, one index row per wave, no
+    # arithmetic) over the same index rows: the rate this access pattern
+    # sustains on the device, at the kernel's eight waves per CU and at as
+    # many waves as the probe's registers allow.
+    probe_out = torch.empty((case.num_rows, 64), dtype=torch.int32, device="cuda")
+    probe = {}
+    ptiles = case.num_rows * ((case.topk + 15) // 16)
+    k2, v2 = k.view(case.kv_len, case.head_dim_qk), v.view(case.kv_len, case.head_dim_v)   # one KV head
+    for name, eight in (("eight_waves_per_cu", True), ("max_waves_per_cu", False)):
+        pms = _events_ms(torch, stream, lambda e=eight: sa.probe_gather(
+            k2, v2, idx, eight_waves=e, out=probe_out, stream=stream), 5, 20)
+        probe[name] = round(ptiles * 16 * 1024 / (pms * 1e-3) / 1e9, 1)
+    probe_gbs = max(probe.values())
+    del probe_out
+
     # The vector L1 bytes the kernel's loads request: every slot tile a team
     # issues loads 16 K rows and 16 V rows (512 B each; invalid slots read a
     # cached row of zeros). Two rows x 6 heads share one 16-column tile.
@@ -740,6 +756,8 @@ def main():
                          if traffic else None),
             "mfma_issued_frac": round(mfma_flops / (kernel_ms * 1e-3) / 1e12
                                       / MFMA_BF16_PEAK_TFLOPS, 4),
+            "gather_probe_GBps": probe,
+            "frac_of_gather_probe": round(l1_gbs / probe_gbs, 4),
         },
         "cpu_baseline": cpu,
         "kernel_ms": round(kernel_ms, 4),

@@ -381,6 +381,25 @@ sa_status sparse_attn_fp8_records_to_bf16(const uint8_t* pool, int64_t pool_row_
 /* Host-only check of an attention descriptor, as sparse_attn_prefill (G=1)
  * or sparse_attn_prefill_union (G>1) would do before launching. Touches no
  * device. Returns SA_OK, SA_OK_FALLBACK (union tile illegal) or an error. */
+/* Measurement aid, not part of the attention path: the K/V row gathers that
+ * the head-dim-256 per-token kernels issue, without their arithmetic, so a
+ * benchmark can compare a kernel's gather rate with what the gather stream
+ * alone sustains on the device. One wavefront per index row walks its slots
+ * in tiles of 16 and reads 512 bytes of K and of V per valid slot in 16-byte
+ * pieces through row buffer descriptors (the attention kernels' loads);
+ * slots outside [0, kv_len) read zeros without touching memory. out[r][l]
+ * is lane l's XOR of the 32-bit words it read for row r.
+ * k, v  device bf16 [kv_len][256], 512-byte rows, kv_len * 512 <= 2^31
+ * idx   device int32 [num_rows][topk], rows contiguous
+ * out   device uint32 [num_rows][64]
+ * eight_waves  1: 64 KB of LDS per four-wave workgroup, so at most eight
+ *       waves per CU (the attention kernels' occupancy); 0: as many as the
+ *       registers allow
+ * Host checks only; no workspace, no host read. */
+sa_status sa_probe_gather(const void* k, const void* v, int32_t kv_len, const int32_t* idx,
+                          int32_t num_rows, int32_t topk, int32_t eight_waves, uint32_t* out,
+                          hipStream_t stream);
+
 int sa_validate_attn(const sa_attn_desc* desc, int32_t G);
 
 /* Message for the calling thread's last error ("" if none). */

@@ -368,3 +368,14 @@ def test_fp8_records_to_bf16_rejects_on_host():
     before = sa.sa_call_count("sparse_attn_fp8_records_to_bf16")
     assert call(n=0, pool=None, out=None) == 0    # nothing to launch, counted
     assert sa.sa_call_count("sparse_attn_fp8_records_to_bf16") == before + 1
+
+
+def test_probe_gather_rejects_on_host():
+    h = sa.lib()
+    null = ctypes.c_void_p(0)
+    shape, null_ptr = -2, -1
+    assert h.sa_probe_gather(null, null, 10, null, 4, 0, 1, null, null) == shape   # topk 0
+    assert h.sa_probe_gather(null, null, 10, null, 4, 8, 2, null, null) == shape   # mode
+    assert h.sa_probe_gather(null, null, 1 << 23, null, 4, 8, 1, null, null) == shape   # > 2 GiB
+    assert h.sa_probe_gather(null, null, 10, null, 4, 8, 1, null, null) == null_ptr
+    assert h.sa_probe_gather(null, null, 10, null, 0, 8, 1, null, null) == sa.SA_OK   # no rows

@@ -117,6 +117,7 @@ _SIGNATURES = {
     "sparse_attn_decode_paged_noalloc": (_I32, [ctypes.POINTER(AttnDesc), ctypes.POINTER(PageDesc),
                                                 _P, _P, _I32, _P, _P, _I32, _P, _P, _P]),
     "sparse_attn_fp8_records_to_bf16": (_I32, [_P, _I64, _I32, _I32, _P, _P, _I64, _P]),
+    "sa_probe_gather": (_I32, [_P, _P, _I32, _P, _I32, _I32, _I32, _P, _P]),
     "sa_validate_attn": (ctypes.c_int, [ctypes.POINTER(AttnDesc), _I32]),
     "sa_last_error": (ctypes.c_char_p, []),
     "sa_call_count": (ctypes.c_uint64, [_I32]),
@@ -451,6 +452,31 @@ def fp8_records_to_bf16(pool: torch.Tensor, *, mask: Optional[torch.Tensor] = No
         _ptr(pool), pool.stride(0) if T else H * 656, T, H, _ptr(mask), _ptr(out),
         out.stride(0) if T else H * 576, _stream(stream))
     _check(st, "sparse_attn_fp8_records_to_bf16")
+    return out
+
+
+def probe_gather(k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, *, eight_waves: bool = True,
+                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Measurement aid (C: sa_probe_gather): the head-dim-256 kernels' K/V
+    row gathers alone. k, v bf16 [kv_len, 256] (contiguous); idx int32
+    [rows, topk] (contiguous). Returns uint32 checksums [rows, 64] (as int32)."""
+    for t, name in ((k, "k"), (v, "v")):
+        _need(t, name, torch.bfloat16, 2)
+        if t.shape[1] != 256 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [kv_len, 256] bf16 tensor")
+    if v.shape[0] != k.shape[0]:
+        raise ValueError("k and v must have the same rows")
+    _need(idx, "idx", torch.int32, 2, k.device)
+    if not idx.is_contiguous():
+        raise ValueError("idx must be contiguous")
+    rows, topk = idx.shape
+    if out is None:
+        out = torch.empty((rows, 64), dtype=torch.int32, device=k.device)
+    _need(out, "out", torch.int32, 2, k.device)
+    _need_size(out, "out", rows, (64,))
+    st = lib().sa_probe_gather(_ptr(k), _ptr(v), k.shape[0], _ptr(idx), rows, topk,
+                               1 if eight_waves else 0, _ptr(out), _stream(stream))
+    _check(st, "sa_probe_gather")
     return out
 
 

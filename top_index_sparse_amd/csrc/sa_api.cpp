@@ -698,4 +698,30 @@ sa_status page_split(const sa_page_desc* desc, const uint8_t* src, uint8_t* dst,
   return ok(SA_ENTRY_PAGE_SPLIT);
 }
 
+sa_status sa_probe_gather(const void* k, const void* v, int32_t kv_len, const int32_t* idx,
+                          int32_t num_rows, int32_t topk, int32_t eight_waves, uint32_t* out,
+                          hipStream_t stream) {
+  if (num_rows < 0 || topk <= 0 || kv_len < 0)
+    return fail(SA_ERR_SHAPE, "num_rows %d, kv_len %d must be >= 0 and topk %d > 0", num_rows,
+                kv_len, topk);
+  if ((int64_t)kv_len * 512 > (1ll << 31))
+    return fail(SA_ERR_SHAPE, "kv_len %d: the rows must lie within 2 GiB", kv_len);
+  if (eight_waves != 0 && eight_waves != 1) return fail(SA_ERR_SHAPE, "eight_waves must be 0 or 1");
+  if (num_rows == 0) return SA_OK;
+  if (!k || !v || !idx || !out) return fail(SA_ERR_NULL, "k, v, idx and out are required");
+  if (!aligned16(k) || !aligned16(v)) return fail(SA_ERR_SHAPE, "k and v must be 16-byte aligned");
+  sa::GatherProbeParams p{};
+  p.k = k;
+  p.v = v;
+  p.idx = idx;
+  p.out = out;
+  p.num_rows = num_rows;
+  p.topk = topk;
+  p.kv_len = kv_len;
+  p.eight_waves = eight_waves;
+  const hipError_t e = sa::launch_gather_probe(p, stream);
+  if (e != hipSuccess) return fail(SA_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return SA_OK;
+}
+
 }  // extern "C"

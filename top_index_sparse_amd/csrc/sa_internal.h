@@ -165,6 +165,17 @@ struct Fp8RowsParams {
 };
 hipError_t launch_fp8_records_to_bf16(const Fp8RowsParams& p, hipStream_t stream);
 
+// sa_probe.hip: the gather stream of the head-dim-256 kernels alone
+struct GatherProbeParams {
+  const void* k;         // [kv_len][256] bf16, 512-byte rows
+  const void* v;
+  const int32_t* idx;    // [num_rows][topk]
+  uint32_t* out;         // [num_rows][64] checksums
+  int32_t num_rows, topk, kv_len;
+  int32_t eight_waves;   // 1: at most eight waves per CU, like the attention kernels
+};
+hipError_t launch_gather_probe(const GatherProbeParams& p, hipStream_t stream);
+
 // sa_api.cpp: the decode entry points' common body (counted under `entry`
 // on success). Without `scratch` it runs over the caller's `ws`; with it,
 // once every argument has passed, over the static scratch of `ws_bytes`
