@@ -373,7 +373,7 @@ struct FastLds : TopkLds {
 // overflow, the row takes the full path instead, so the result never
 // depends on the sample.
 constexpr int kLevelBins = 2048;   // 11 bits per level
-constexpr int kSCap = 6144;        // candidate list capacity (about k + 30 % in practice)
+constexpr int kSCap = 6144;        // candidate list capacity (C1topk: about 1.6 k)
 constexpr int kSampleMaxK = 4096;
 constexpr int kSmall = 64;         // a bin this small is ranked by one wave
 
@@ -388,14 +388,15 @@ struct SampledLds {
   uint32_t tieb[kWords];          // tied at the final threshold, by position
   uint32_t red2[2 * kWaves];
   uint32_t ncand;
-  uint32_t hi;                    // the row's largest key (a bound, below +0)
+  uint32_t hi;                    // the row's largest key (above +0; else the largest key there is)
   uint32_t found[4];
   uint32_t nsmall;                // a threshold bin of at most kSmall candidates, ranked whole
   uint32_t skey[kSmall];
   uint32_t spos[kSmall];
 };
 
-// Largest value over the wave's lanes, in lane 63 (DPP steps as wave_scan64).
+// Largest value over the wave's lanes (the DPP steps of wave_scan64 with max;
+// lane 63 ends with it), in every lane.
 __device__ __forceinline__ uint32_t wave_max64(uint32_t x) {
   x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true));   // row_shr:1
   x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true));   // row_shr:2
@@ -409,7 +410,7 @@ __device__ __forceinline__ uint32_t wave_max64(uint32_t x) {
 // One wave: over nb bins of h (a power of two, at most 2048), with need
 // = need_of(total count), the bin holding the need-th largest counted from
 // the top bin down. found: the bin, how many of it are needed, whether that
-// is all of it. Lane l sums bins [nb - per (l+1), nb - per l); the lane
+// is all of it, and its count. Lane l sums bins [nb - per (l+1), nb - per l); the lane
 // holding the need-th then has its bins spread over the wave.
 template <int UNROLL, typename NeedOf>
 __device__ __forceinline__ void wave_find(const uint32_t* h, int nb, NeedOf need_of, uint32_t* found) {
