@@ -59,8 +59,10 @@
 //   (log2 units), so the O^T rescale is rare; probabilities up to 2^kSlack
 //   are exact in fp32 and bf16 rounding is relative, so nothing is lost.
 //   MLA (V inside the 576-wide latent row): each wavefront gathers its V
-//   columns plus its rope columns as one slice through LDS and reads both
-//   operands from there.
+//   columns plus its rope columns and stages the slice in LDS for S^T. With
+//   row descriptors the latent chunks are gathered in the V operand's order
+//   and serve as V from the registers; the 64-bit path and FP8 records read
+//   V back from the staged slice.
 //
 // Invalid slots (outside [0, kv_len), past topk or topk_len, or owned by
 // none of the team's rows) read zeros (a row index the buffer descriptor's
@@ -162,6 +164,14 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   constexpr bool DECODE = MODE == kDecode;
   constexpr bool MEMBER = MODE == kRowsMember;
   constexpr bool VKLDS = TT::VKLDS;
+  // V inside K, gathered through row descriptors: lane (g, n) reads latent
+  // chunks n and 16 + n of slots 4g .. 4g+3 (the V operand's order, as for a
+  // separate V) plus rope chunk n % 4 of slot 4g + n / 4; the chunks are
+  // staged for S^T and the latent ones kept in registers as V, so LDS
+  // carries only the S^T transpose.
+  constexpr bool VDIRECT = VKLDS && BUF && !FP8;
+  static_assert(!VDIRECT || (TT::MAIN == 256 && TT::ROPE == 32 && TT::VCH == 2 && KSTEPS == 9),
+                "direct V: 32 latent and 4 rope chunks per slot and wave");
   constexpr int KCH = TT::KCH;
   constexpr int KROW = TT::KROW;
   constexpr int MAIN = TT::MAIN;
@@ -464,6 +474,14 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
         for (int i = 0; i < 4; ++i) td.kd[i] = ld_row16(rk, rw[i], 256 * split + 16 * n);
         td.kd[4] = ld_row16(rk, pick(rw, ir), 528 + 64 * split + 16 * is);
         td.kd[5] = ld_row16(rk, pick(rw, is), 512);
+      } else if constexpr (VDIRECT) {
+        auto pick = [](const int a[4], int i) { return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3]; };
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int h = 0; h < VCH; ++h)
+            td.kd[VCH * i + h] = ld_row16(rk, rw[i], 2 * split * MAIN + 256 * h + 16 * n);
+        td.kd[4 * VCH] = ld_row16(rk, pick(rw, n >> 2), 2 * (DV + split * ROPE) + 16 * (n & 3));
       } else if constexpr (VKLDS) {
 #pragma unroll
         for (int q = 0; q < KSTEPS; ++q) {
@@ -610,6 +628,15 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
         *reinterpret_cast<u32x4_t*>(row + cpos(2 * n + 1)) = (u32x4_t){b[4], b[5], b[6], b[7]};
       }
       *reinterpret_cast<u32x4_t*>(lk + (4 * g + (n >> 2)) * KROW + 16 * (MAIN / 8 + (n & 3))) = td.kd[4];
+    } else if constexpr (VDIRECT) {
+      // latent chunk 16h + n of slot 4g+i, rope chunk n % 4 of slot 4g + n/4
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < VCH; ++h)
+          *reinterpret_cast<u32x4_t*>(lk + (4 * g + i) * KROW + 16 * (16 * h + n)) = td.kd[VCH * i + h];
+      *reinterpret_cast<u32x4_t*>(lk + (4 * g + (n >> 2)) * KROW + 16 * (MAIN / 8 + (n & 3))) =
+          td.kd[4 * VCH];
     } else if constexpr (VKLDS) {
       // chunk c = 16q + n of group g's slots (the gather's order)
 #pragma unroll
@@ -688,8 +715,9 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int h = 0; h < VCH; ++h)
-        vv[VCH * i + h] = VKLDS ? *reinterpret_cast<const u32x4_t*>(lk + (4 * g + i) * KROW + cpos(16 * h + n))
-                                : td.vd[VCH * i + h];
+        vv[VCH * i + h] = VDIRECT ? td.kd[VCH * i + h]
+                          : VKLDS ? *reinterpret_cast<const u32x4_t*>(lk + (4 * g + i) * KROW + cpos(16 * h + n))
+                                  : td.vd[VCH * i + h];
 #pragma unroll
     for (int mt = 0; mt < MTILES; ++mt) {
       const int h = mt >> 3, e = mt & 7;
