@@ -409,6 +409,10 @@ def measure_others(args, sa, torch, stream):
             q, k, None, idx, G, sm_scale=c.scale, head_dim_v=512, ws=ws, out=out, lse=lse,
             stream=stream), w, n)
         r = _rate(rows * 1152, ms_all)
+        # (build_ms times the public build, which also writes the -1 / 0 tail
+        # of every list; the build inside the union call does not, so
+        # attention_ms = total - build_ms reads about 2 % low: the kernel
+        # trace gives the exact split)
         r.update({"union_rows": rows, "build_ms": round(ms_build, 4),
                   "attention_ms": round(ms_all - ms_build, 4),
                   "per_token_equivalent_GBps": round(per_token_bytes / (ms_all * 1e-3) / 1e9, 1),
