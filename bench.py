@@ -317,6 +317,8 @@ def measure_others(args, sa, torch, stream):
     ms_all = _events_ms(torch, stream, lambda: sa.sparse_attn_prefill_union(
         q, k, v, idx, 2, sm_scale=c.scale, ws=ws, out=out, lse=lse, stream=stream), w, n)
     r = _rate(rows * 1024, ms_all)
+    # (attention_ms = total - the public build, which also writes the lists'
+    # -1 / 0 tails: a little low, as for the MLA union below)
     r.update({"union_rows": rows, "build_ms": round(ms_build, 4),
               "attention_ms": round(ms_all - ms_build, 4),
               "per_token_equivalent_GBps": round(per_token_bytes / (ms_all * 1e-3) / 1e9, 1)})
