@@ -61,8 +61,9 @@
 //   MLA (V inside the 576-wide latent row): each wavefront gathers its V
 //   columns plus its rope columns and stages the slice in LDS for S^T. With
 //   row descriptors the latent chunks are gathered in the V operand's order
-//   and serve as V from the registers; the 64-bit path and FP8 records read
-//   V back from the staged slice.
+//   and serve as V from the registers (FP8 records in per-token teams: their
+//   codes, dequantised in registers); the 64-bit path and the FP8 union team
+//   read V back from the staged slice.
 //
 // Invalid slots (outside [0, kv_len), past topk or topk_len, or owned by
 // none of the team's rows) read zeros (a row index the buffer descriptor's
@@ -170,6 +171,10 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   // staged for S^T and the latent ones kept in registers as V, so LDS
   // carries only the S^T transpose.
   constexpr bool VDIRECT = VKLDS && BUF && !FP8;
+  // FP8 records, per-token teams: the codes of chunks n and 16 + n, dequantised
+  // in registers, staged for S^T and kept as V (the three-wave union team
+  // would spill the extra registers, so it reads V back from the slice)
+  constexpr bool FP8DIRECT = FP8 && BUF && MODE != kUnion;
   static_assert(!VDIRECT || (TT::MAIN == 256 && TT::ROPE == 32 && TT::VCH == 2 && KSTEPS == 9),
                 "direct V: 32 latent and 4 rope chunks per slot and wave");
   constexpr int KCH = TT::KCH;
@@ -470,8 +475,17 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
         // as below: latent half rows, one rope chunk, the slot's scales
         const int ir = n >> 2, is = n & 3;
         auto pick = [](const int a[4], int i) { return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3]; };
+        if constexpr (FP8DIRECT) {   // codes of chunks n and 16 + n, 8 bytes each
 #pragma unroll
-        for (int i = 0; i < 4; ++i) td.kd[i] = ld_row16(rk, rw[i], 256 * split + 16 * n);
+          for (int i = 0; i < 4; ++i) {
+            const u32x2_t a = ld_row8(rk, rw[i], 256 * split + 8 * n);
+            const u32x2_t b = ld_row8(rk, rw[i], 256 * split + 128 + 8 * n);
+            td.kd[i] = (u32x4_t){a[0], a[1], b[0], b[1]};
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) td.kd[i] = ld_row16(rk, rw[i], 256 * split + 16 * n);
+        }
         td.kd[4] = ld_row16(rk, pick(rw, ir), 528 + 64 * split + 16 * is);
         td.kd[5] = ld_row16(rk, pick(rw, is), 512);
       } else if constexpr (VDIRECT) {
@@ -600,9 +614,10 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
   // (c + b) mod 8): the pair writes, the V reads (chunk 16h + n of lane n)
   // and the A-operand reads all stay free of bank conflicts.
   auto cpos = [](int c) {
-    return 16 * (FP8 && c < 32 ? (c & ~7) | ((c + (c >> 3)) & 7) : c);
+    return 16 * (FP8 && !FP8DIRECT && c < 32 ? (c & ~7) | ((c + (c >> 3)) & 7) : c);
   };
   auto compute = [&](const Data& td, const int own[4]) {
+    u32x4_t vdq[FP8DIRECT ? 8 : 1];   // FP8DIRECT: the dequantised latent chunks n, 16 + n (V)
     // Stage the gathered rows in LDS, in the A-operand order.
     if constexpr (FP8) {
       // Dequantise: latent chunk n of slot 4g+i (values 16n .. 16n+15 of the
@@ -614,6 +629,25 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
       quad_bcast4((int)td.kd[5][2 * split + 1], s1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        if constexpr (FP8DIRECT) {
+          // words 0-1: codes of chunk n (block 2 split), words 2-3: chunk 16 + n
+          const float sa = __builtin_bit_cast(float, s0[i]), sb = __builtin_bit_cast(float, s1[i]);
+          uint32_t b[8];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float sc = w < 2 ? sa : sb;
+            const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)td.kd[i][w], false);
+            const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)td.kd[i][w], true);
+            b[2 * w] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
+            b[2 * w + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
+          }
+          vdq[2 * i] = (u32x4_t){b[0], b[1], b[2], b[3]};
+          vdq[2 * i + 1] = (u32x4_t){b[4], b[5], b[6], b[7]};
+          uint8_t* row = lk + (4 * g + i) * KROW;
+          *reinterpret_cast<u32x4_t*>(row + 16 * n) = vdq[2 * i];
+          *reinterpret_cast<u32x4_t*>(row + 16 * (16 + n)) = vdq[2 * i + 1];
+          continue;
+        }
         const float sc = __builtin_bit_cast(float, (n >> 3) ? s1[i] : s0[i]);
         uint32_t b[8];
 #pragma unroll
@@ -715,7 +749,8 @@ __device__ __forceinline__ void attn_team(const AttnParams& p, int team_id, int 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int h = 0; h < VCH; ++h)
-        vv[VCH * i + h] = VDIRECT ? td.kd[VCH * i + h]
+        vv[VCH * i + h] = FP8DIRECT ? vdq[FP8DIRECT ? VCH * i + h : 0]
+                          : VDIRECT ? td.kd[VCH * i + h]
                           : VKLDS ? *reinterpret_cast<const u32x4_t*>(lk + (4 * g + i) * KROW + cpos(16 * h + n))
                                   : td.vd[VCH * i + h];
 #pragma unroll

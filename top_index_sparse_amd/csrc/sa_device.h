@@ -68,6 +68,12 @@ __device__ __forceinline__ rows_rsrc_t rows_rsrc(const void* base, uint32_t stri
                                            0x00020000);
 }
 
+__device__ u32x2_t sa_struct_buffer_load_v2(rows_rsrc_t r, int row, int off, int soff, int aux)
+    __asm("llvm.amdgcn.struct.ptr.buffer.load.v2i32");
+__device__ __forceinline__ u32x2_t ld_row8(rows_rsrc_t r, int row, int off) {
+  return sa_struct_buffer_load_v2(r, row, off, 0, 0);
+}
+
 __device__ __forceinline__ u32x4_t ld_row16(rows_rsrc_t r, int row, int off) {
   return sa_struct_buffer_load_v4(r, row, off, 0, 0);
 }
