@@ -136,3 +136,35 @@ def test_topk_sample_misleads(kv):
         _check(s, k, None, f"kv={kv} k={k} planted")
         _check(s, k, np.array([kv, kv - 5, kv // 2 + 3, 4 * k // 3 + 1], np.int32),
                f"kv={kv} k={k} planted, lengths")
+
+
+@pytest.mark.parametrize("kv", [8192, 20000, 32764])
+def test_topk_sampled_row_ends(kv):
+    """Rows of N(0,1) scores over storage of a multiple of four scores (the
+    16-byte read of every chunk, lanes past the row reading the quad that
+    holds its last position): lengths that end inside a quad, inside a
+    chunk and chunks before the storage ends, with large scores stored past
+    every row's end, where a missed mask would select them."""
+    say(f"[topk] kv {kv}: sampled selection, row ends inside quads and chunks")
+    rng = np.random.default_rng(kv + 11)
+    lengths = [kv, kv - 1, kv - 3, 4097, 4099, kv // 2 + 1, kv // 2 + 2, 5 * kv // 8 + 3]
+    s = rng.standard_normal((len(lengths), kv)).astype(np.float32)
+    rl = np.array(lengths, np.int32)
+    for t, n in enumerate(lengths):
+        s[t, n:] = 50.0
+    for k in (1, 777, 2051, 4096):
+        _check(s, k, rl, f"kv={kv} k={k} row ends")
+
+
+def test_topk_odd_row_stride():
+    """A row stride of an odd number of floats leaves most rows unaligned
+    for 16-byte loads: the selection must not depend on it."""
+    say("[topk] scores with an odd row stride")
+    rng = np.random.default_rng(6)
+    T, kv, k = 6, 20000, 2051
+    buf = rng.standard_normal((T, kv + 3)).astype(np.float32)
+    sc = torch.from_numpy(buf).cuda()[:, :kv]
+    rl = np.array([kv, kv - 1, 9001, 4097, 2052, 19999], np.int32)
+    got = sa.indexer_topk(sc, k, row_len=i32_dev(rl))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), oracle.topk_select(buf[:, :kv], k, rl))
