@@ -393,6 +393,7 @@ struct SampledLds {
   uint32_t nsmall;                // a threshold bin of at most kSmall candidates, ranked whole
   uint32_t skey[kSmall];
   uint32_t spos[kSmall];
+  uint32_t smax, scount;          // the sample's largest key and its count
 };
 
 // Largest value over the wave's lanes (the DPP steps of wave_scan64 with max;
@@ -475,6 +476,8 @@ __device__ __forceinline__ bool sampled_select(SampledLds<PER>& S, int n, uint32
     S.ncand = 0u;
     S.hi = 0u;
     S.nsmall = 0u;
+    S.smax = 0u;
+    S.scount = 0u;
   }
   // sample: position 4 (c kThreads + tid) of chunk c = tid mod NCH
   const int cs = tid & (NCH - 1);
@@ -490,14 +493,46 @@ __device__ __forceinline__ bool sampled_select(SampledLds<PER>& S, int n, uint32
   const uint32_t skey = 4 * (cs * kThreads + tid) < n ? score_key(sraw) : 0u;
   __syncthreads();
   if (skey) atomicAdd(&S.hist[0][skey >> 21], 1u);
+  {
+    const uint32_t wmax = wave_max64(skey);
+    const uint32_t wcnt = (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(skey != 0u));
+    if (lane == 0) {
+      atomicMax(&S.smax, wmax);
+      atomicAdd(&S.scount, wcnt);
+    }
+  }
   __syncthreads();
   if (wv == 0) {
     const float pk = (float)k / (float)n;
-    wave_find<1>(S.hist[0], kLevelBins, [&](uint32_t ns) {
+    auto need_of = [&](uint32_t ns) {
       const float mean = (float)ns * pk;
       const uint32_t r = (uint32_t)ceilf(mean + 4.f * sqrtf(mean * (1.f - pk)) + 4.f);
       return r < ns ? r : ns;
-    }, S.found);
+    };
+    // The bin sought is usually a few below the sample's largest: lane l
+    // takes bin top - l, and one scan finds it among those 64; otherwise
+    // the search over all 2048 bins.
+    const int topb = (int)(S.smax >> 21);
+    const uint32_t total = S.scount;
+    uint32_t need = need_of(total);
+    need = need < total ? need : total;
+    const int b = topb - lane;
+    const uint32_t c = b >= 0 ? S.hist[0][b & (kLevelBins - 1)] : 0u;
+    const uint32_t incl = wave_scan64(c);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(incl >= need);
+    if (hit) {   // uniform
+      const int M = __builtin_ctzll(hit);
+      const uint32_t cM = (uint32_t)__builtin_amdgcn_readlane((int)c, M);
+      const uint32_t before = (uint32_t)__builtin_amdgcn_readlane((int)incl, M) - cM;
+      if (lane == 0) {
+        S.found[0] = (uint32_t)(topb - M);
+        S.found[1] = need - before;
+        S.found[2] = cM == need - before;
+        S.found[3] = cM;
+      }
+    } else {
+      wave_find<1>(S.hist[0], kLevelBins, need_of, S.found);
+    }
   }
   __syncthreads();
   uint32_t tk = S.found[0] << 21;
