@@ -168,3 +168,23 @@ def test_topk_odd_row_stride():
     got = sa.indexer_topk(sc, k, row_len=i32_dev(rl))
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy(), oracle.topk_select(buf[:, :kv], k, rl))
+
+
+@pytest.mark.parametrize("kv", [16384, 32768])
+def test_topk_sample_outliers(kv):
+    """A few huge scores at sampled positions put the sample's largest key
+    far above the bin its threshold lies in, beyond the 64 bins the short
+    search scans below it, so the threshold comes from the search over all
+    bins; the selection must not change."""
+    say(f"[topk] kv {kv}: outliers at sampled positions")
+    rng = np.random.default_rng(kv + 17)
+    s = rng.standard_normal((4, kv)).astype(np.float32)
+    pos = _sample_positions(kv)
+    s[0, pos[:3]] = 1e30
+    s[1, pos[::97]] = np.float32(3e38)
+    s[2, pos[:1]] = 1e10
+    s[3, pos[:40]] = 1e20 * rng.random(40).astype(np.float32)
+    for k in (1, 64, 2051, 4096):
+        _check(s, k, None, f"kv={kv} k={k} outliers")
+        _check(s, k, np.array([kv, kv - 7, kv // 2 + 5, 3 * k // 2 + 1], np.int32),
+               f"kv={kv} k={k} outliers, lengths")
