@@ -1,9 +1,10 @@
 """Union-of-G index sets and union attention in fp64 (TEST INFRASTRUCTURE:
 oracle only).
 
-sglang PR 32779, "Modifications" (``--dsa-triton-union``): G adjacent tokens
-share one gathered index set; a per-row ownership bitmask restores each
-token's own softmax support, so the result equals the per-token path. The set
+sglang PR 32779, "Modifications" (``--dsa-triton-union``): a group of G
+neighbouring tokens gathers one common index set, and each gathered row
+carries bits naming the tokens that selected it, so every token's softmax
+runs over its own rows only and the output matches per-token attention. The set
 is built per group: each token's rows are sorted on their own; a row goes
 into the set under the first token of the group that holds it, and its bits
 mark every token of the group that holds it. "Accuracy Tests" states the
