@@ -4,10 +4,10 @@ oracle only).
 sglang PR 32779, "Modifications" (``--dsa-triton-union``): a group of G
 neighbouring tokens gathers one common index set, and each gathered row
 carries bits naming the tokens that selected it, so every token's softmax
-runs over its own rows only and the output matches per-token attention. The set
-is built per group: each token's rows are sorted on their own; a row goes
-into the set under the first token of the group that holds it, and its bits
-mark every token of the group that holds it. "Accuracy Tests" states the
+runs over its own rows only and the output matches per-token attention. Each
+group's set is formed by sorting every member's rows separately; a row enters
+the set under the first member that selected it, and its bits name every
+member that selected it. "Accuracy Tests" states the
 contract the tests check: no row appears twice, a row's bits are the union
 of its holders' bits, and -1 slots are left out.
 

@@ -260,7 +260,7 @@ def check_union_contract(union_build, seed=7):
 
 def check_union_equals_per_token(union_attention, sparse_attention, union_build, seed=8):
     """With duplicate-free rows, union attention equals per-token attention
-    (PR 32779: the result is identical to the per-token path)."""
+    (PR 32779: union mode must reproduce the per-token output)."""
     for (T, G, Hq) in [(12, 2, 4), (11, 4, 8), (5, 3, 2)]:
         kv, width, D = 30, 9, 16
         rng, q, k, _ = _case(seed + T, T, kv, Hq, 1, D, 8, v_in_k=True)
