@@ -3,7 +3,7 @@
 // decode kernel reads pages of dst_page_tokens. The mark pass flags every
 // source page that a valid token index of the step falls in; the split pass
 // runs a fixed grid of one workgroup per destination page and returns at once
-// when its source page is unflagged, so only touched pages are copied and
+// when its source page is unflagged: untouched pages cost one flag read, and
 // the launch shape never depends on the data (no host read, graph safe).
 #include "sa_device.h"
 #include "sa_internal.h"

@@ -1,10 +1,9 @@
 // Union-of-G index sets on the device (sglang PR 32779, "Modifications",
-// --dsa-triton-union): each row's selected indices are sorted on their own,
-// then one workgroup per group of G adjacent rows runs a lower_bound of every
-// index against the other rows' sorted lists. A row emits an index iff no
-// earlier row of the group selected it, and every row that selected it sets
-// its ownership bit. Nothing is read back to the host and nothing outlives
-// the call.
+// --dsa-triton-union). For each group of G neighbouring rows the output
+// lists every distinct valid index once, under the lowest member row that
+// selected it, with one ownership bit per member row that selected it. Two
+// builders below produce the same bytes; neither reads anything back to the
+// host or keeps state between calls.
 //
 // Output layout (bit-exact, deterministic): union_idx[g] lists row 0's
 // distinct valid indices ascending, then row 1's new ones ascending, ...,
