@@ -159,11 +159,13 @@ size_t sparse_attn_union_workspace_bytes(int32_t num_rows, int32_t topk, int32_t
 
 /* Union-of-G index sets (sglang PR 32779, "Modifications",
  * --dsa-triton-union): rows g*G .. g*G+G-1 form group g (the last group may
- * be short). A row emits an index iff no earlier row of its group selected
- * it; every row that selected it sets its ownership bit (bit j = j-th row
- * of the group). The page sorts each row and runs a lower_bound merge; here
- * that path serves G x kv_len > 2^19, and smaller groups are built from one
- * LDS bit plane per row over [0, kv_len) instead. Both give the same output.
+ * be short). Each distinct valid index of a group is listed once, under
+ * the lowest member row that selected it, and carries one ownership bit per
+ * member that selected it (bit j = j-th row of the group). The page builds
+ * the set by sorting each row and searching the other rows' sorted lists;
+ * here that path serves G x kv_len > 2^19, and smaller groups are built from
+ * one LDS bit plane per row over [0, kv_len) instead. Both give the same
+ * output.
  *
  * idx         device int32 [num_rows][topk], row stride idx_row_stride
  * union_idx   device int32 [ceil(num_rows/G)][G*topk]: row 0's distinct
