@@ -152,7 +152,7 @@ def test_topk_sampled_row_ends(kv):
     rl = np.array(lengths, np.int32)
     for t, n in enumerate(lengths):
         s[t, n:] = 50.0
-    for k in (1, 777, 2051, 4096):
+    for k in (1, 777, 2051, 4096, 4097):   # (4097: past the sampled selection's k)
         _check(s, k, rl, f"kv={kv} k={k} row ends")
 
 
@@ -184,7 +184,7 @@ def test_topk_sample_outliers(kv):
     s[1, pos[::97]] = np.float32(3e38)
     s[2, pos[:1]] = 1e10
     s[3, pos[:40]] = 1e20 * rng.random(40).astype(np.float32)
-    for k in (1, 64, 2051, 4096):
+    for k in (1, 64, 2051, 4096, 4097):
         _check(s, k, None, f"kv={kv} k={k} outliers")
         _check(s, k, np.array([kv, kv - 7, kv // 2 + 5, 3 * k // 2 + 1], np.int32),
                f"kv={kv} k={k} outliers, lengths")
